@@ -1,0 +1,250 @@
+"""Seeded synthetic inputs for paged GQA decode and sparse prefill.
+
+This module only draws random numbers and arranges them in memory; it holds
+none of the attention arithmetic.  The fp64 oracle and the GPU library both
+consume what it returns, so it imports neither of them.
+
+Recipes (page sections cited by title):
+  - Decode ("[Kernel][SM70] Scale NVFP4 E4M3 decode batches", Purpose and
+    Performance contract): 6 query heads per KV head, head dim 256, batches of
+    1-16 sequences with 1K-16K context, FP8-E4M3 KV.  q, K and V are drawn
+    from N(0, 1); FP8 KV holds the round-to-nearest-even E4M3 codes of those
+    draws (torch's CPU float8_e4m3fn cast), FP16 the binary16 rounding.
+  - Sparse prefill ("[Kernel][SM70] Accelerate Qwen3.8 QSA paged prefill",
+    Changes): each row selects 4-aligned blocks of a shared KV pool; its
+    virtual page-4 table lists the selected blocks in increasing order
+    (locality-sorted) followed by the causal partial page.
+Seeds: ``numpy.random.SeedSequence(seed).spawn(6)`` children are used, in this
+order, for q, K, V, the page tables, the scales and the lengths.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+KV_FP16 = 0
+KV_E4M3 = 1
+LAYOUTS = ("contiguous", "interleaved", "head_major")
+
+
+def quantize_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to OCP E4M3FN codes (uint8) with torch's CPU cast
+    (round to nearest, ties to even).  Callers keep |x| < 448."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@dataclass
+class PagedCase:
+    """One paged-attention problem held in host memory."""
+
+    q: np.ndarray                 # float16 [n][Hq][D]
+    k_store: np.ndarray           # pool storage holding K (uint8 codes or float16)
+    v_store: np.ndarray           # pool storage holding V (may be k_store itself)
+    k_offset: int                 # element offset of K(page 0, slot 0, head 0, dim 0)
+    v_offset: int
+    page_stride: int              # strides in elements
+    token_stride: int
+    head_stride: int
+    num_pages: int
+    page_size: int
+    kv_dtype: int                 # KV_FP16 or KV_E4M3
+    k_scale: float
+    v_scale: float
+    table: np.ndarray             # int32 [n][max_pages]
+    lens: np.ndarray              # int32 [n]
+    max_seq_len: int
+    sm_scale: float
+    num_kv_heads: int
+    layout: str
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def n(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def num_q_heads(self) -> int:
+        return self.q.shape[1]
+
+    @property
+    def head_dim(self) -> int:
+        return self.q.shape[2]
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        return 2 if self.kv_dtype == KV_FP16 else 1
+
+    def kv_bytes_read(self) -> int:
+        """Algorithmic KV bytes one call must read: every live token's K and V
+        row for every KV head, read once."""
+        live = np.clip(self.lens.astype(np.int64), 0, self.max_seq_len).sum()
+        return int(live) * self.num_kv_heads * self.head_dim * self.kv_elem_bytes * 2
+
+    def oracle_kwargs(self) -> dict:
+        return dict(q=self.q, k_store=self.k_store, v_store=self.v_store,
+                    k_offset=self.k_offset, v_offset=self.v_offset,
+                    page_stride=self.page_stride, token_stride=self.token_stride,
+                    head_stride=self.head_stride, num_pages=self.num_pages,
+                    page_size=self.page_size, kv_dtype=self.kv_dtype,
+                    k_scale=self.k_scale, v_scale=self.v_scale, table=self.table,
+                    lens=self.lens, sm_scale=self.sm_scale,
+                    num_kv_heads=self.num_kv_heads)
+
+
+def _values(rng: np.random.Generator, shape, kv_dtype: int) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if kv_dtype == KV_E4M3:
+        return quantize_e4m3(x)
+    return x.astype(np.float16)
+
+
+def build_pool(kvals: np.ndarray, vvals: np.ndarray, layout: str) -> dict:
+    """Lay out K and V page contents ([num_pages][P][Hkv][D] each) as a pool.
+
+    contiguous : separate K and V arrays [num_pages][P][Hkv][D]
+    interleaved: one array [num_pages][2][P][Hkv][D] (K block, then V block)
+    head_major : separate arrays [num_pages][Hkv][P][D]
+    """
+    npg, P, hkv, d = kvals.shape
+    if layout == "contiguous":
+        return dict(k_store=np.ascontiguousarray(kvals), v_store=np.ascontiguousarray(vvals),
+                    k_offset=0, v_offset=0, page_stride=P * hkv * d,
+                    token_stride=hkv * d, head_stride=d)
+    if layout == "interleaved":
+        store = np.empty((npg, 2, P, hkv, d), dtype=kvals.dtype)
+        store[:, 0] = kvals
+        store[:, 1] = vvals
+        return dict(k_store=store, v_store=store, k_offset=0, v_offset=P * hkv * d,
+                    page_stride=2 * P * hkv * d, token_stride=hkv * d, head_stride=d)
+    if layout == "head_major":
+        return dict(k_store=np.ascontiguousarray(kvals.transpose(0, 2, 1, 3)),
+                    v_store=np.ascontiguousarray(vvals.transpose(0, 2, 1, 3)),
+                    k_offset=0, v_offset=0, page_stride=P * hkv * d,
+                    token_stride=d, head_stride=P * d)
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def decode_case(*, batch: int, lens, page_size: int, kv_dtype: int,
+                layout: str = "contiguous", seed: int = 0, num_q_heads: int = 6,
+                num_kv_heads: int = 1, head_dim: int = 256, scales="unit",
+                table: str = "perm", num_pages: int | None = None,
+                max_seq_len: int | None = None, sm_scale: float | None = None) -> PagedCase:
+    """Paged decode problem.
+
+    lens   : int (all sequences) or a sequence of ints, or ("uniform", lo, hi)
+             for lengths drawn uniformly on [lo, hi] from the lengths stream.
+    scales : "unit" (1.0, 1.0), "uniform" (each ~ U[0.5, 2]) or a (k, v) pair.
+    table  : "perm"  - the pool holds exactly batch*max_pages pages and the
+                       tables are a random permutation of them, reshaped;
+             "identity" - sequence b owns pages b*max_pages .. in order.
+    """
+    ss = np.random.SeedSequence(seed).spawn(6)
+    rq, rk, rv, rt, rs, rl = (np.random.default_rng(s) for s in ss)
+    if isinstance(lens, tuple) and lens and lens[0] == "uniform":
+        lens_arr = rl.integers(lens[1], lens[2], size=batch, endpoint=True).astype(np.int32)
+    elif np.isscalar(lens):
+        lens_arr = np.full(batch, int(lens), dtype=np.int32)
+    else:
+        lens_arr = np.asarray(lens, dtype=np.int32)
+        assert lens_arr.shape == (batch,)
+    if max_seq_len is None:
+        max_seq_len = max(1, int(lens_arr.max(initial=0)))
+    max_pages = -(-max_seq_len // page_size)
+    if num_pages is None:
+        num_pages = batch * max_pages
+    if table == "perm":
+        assert num_pages >= batch * max_pages
+        tab = rt.permutation(num_pages)[: batch * max_pages].reshape(batch, max_pages)
+    elif table == "identity":
+        assert num_pages >= batch * max_pages
+        tab = np.arange(batch * max_pages).reshape(batch, max_pages)
+    else:
+        raise ValueError(table)
+    if scales == "unit":
+        k_scale, v_scale = 1.0, 1.0
+    elif scales == "uniform":
+        k_scale, v_scale = (float(s) for s in rs.uniform(0.5, 2.0, size=2))
+    else:
+        k_scale, v_scale = (float(s) for s in scales)
+    q = rq.standard_normal((batch, num_q_heads, head_dim), dtype=np.float32).astype(np.float16)
+    shape = (num_pages, page_size, num_kv_heads, head_dim)
+    pool = build_pool(_values(rk, shape, kv_dtype), _values(rv, shape, kv_dtype), layout)
+    return PagedCase(q=q, **pool, num_pages=num_pages, page_size=page_size,
+                     kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale,
+                     table=np.ascontiguousarray(tab, dtype=np.int32), lens=lens_arr,
+                     max_seq_len=int(max_seq_len),
+                     sm_scale=(1.0 / np.sqrt(head_dim)) if sm_scale is None else sm_scale,
+                     num_kv_heads=num_kv_heads, layout=layout)
+
+
+def sparse_prefill_case(*, rows: int, selected_blocks: int, tail: int, pool_blocks: int,
+                        layout: str = "interleaved", seed: int = 0, num_q_heads: int = 6,
+                        num_kv_heads: int = 1, head_dim: int = 256,
+                        kv_dtype: int = KV_FP16, scales="unit") -> PagedCase:
+    """Sparse prefill through virtual page-4 tables.
+
+    Row r owns block c_r = pool_blocks - rows + r (its causal block).  It
+    selects `selected_blocks` distinct blocks uniformly from [0, c_r), sorted
+    increasingly (locality order), then the partial page: the first `tail`
+    tokens of block c_r (tail = 0 means no partial page).  Row length is
+    4*selected_blocks + tail.
+    """
+    P = 4
+    assert 0 <= tail < P and pool_blocks - rows >= selected_blocks
+    ss = np.random.SeedSequence(seed).spawn(6)
+    rq, rk, rv, rt, rs, _ = (np.random.default_rng(s) for s in ss)
+    n_entries = selected_blocks + (1 if tail else 0)
+    tab = np.empty((rows, n_entries), dtype=np.int32)
+    for r in range(rows):
+        c_r = pool_blocks - rows + r
+        sel = rt.choice(c_r, size=selected_blocks, replace=False, shuffle=False)
+        tab[r, :selected_blocks] = np.sort(sel)
+        if tail:
+            tab[r, selected_blocks] = c_r
+    L = P * selected_blocks + tail
+    if scales == "unit":
+        k_scale, v_scale = 1.0, 1.0
+    elif scales == "uniform":
+        k_scale, v_scale = (float(s) for s in rs.uniform(0.5, 2.0, size=2))
+    else:
+        k_scale, v_scale = (float(s) for s in scales)
+    q = rq.standard_normal((rows, num_q_heads, head_dim), dtype=np.float32).astype(np.float16)
+    shape = (pool_blocks, P, num_kv_heads, head_dim)
+    pool = build_pool(_values(rk, shape, kv_dtype), _values(rv, shape, kv_dtype), layout)
+    return PagedCase(q=q, **pool, num_pages=pool_blocks, page_size=P, kv_dtype=kv_dtype,
+                     k_scale=k_scale, v_scale=v_scale, table=tab,
+                     lens=np.full(rows, L, dtype=np.int32), max_seq_len=L,
+                     sm_scale=1.0 / np.sqrt(head_dim), num_kv_heads=num_kv_heads,
+                     layout=layout, meta=dict(selected_blocks=selected_blocks, tail=tail))
+
+
+# The five workloads, by what they are.
+WORKLOADS = {
+    "decode_b1_1k_fp16_p16": dict(kind="decode", batch=1, lens=1024, page_size=16,
+                                   kv_dtype=KV_FP16, layout="contiguous", seed=0,
+                                   sm_scale=1.0 / 16),
+    "decode_b8_1k_e4m3_p64": dict(kind="decode", batch=8, lens=1024, page_size=64,
+                                   kv_dtype=KV_E4M3, layout="contiguous", seed=0),
+    "decode_b16_16k_e4m3_p128": dict(kind="decode", batch=16, lens=16384, page_size=128,
+                                      kv_dtype=KV_E4M3, layout="contiguous", seed=0,
+                                      scales="uniform"),
+    "decode_ragged_b16_16k_p256": dict(kind="decode", batch=16, lens=("uniform", 1, 16384),
+                                        page_size=256, max_seq_len=16384, seed=0),
+    "prefill_sparse_4096x2051_p4": dict(kind="prefill", rows=4096, selected_blocks=512,
+                                         tail=3, pool_blocks=65536, layout="interleaved",
+                                         seed=0),
+}
+
+
+def workload_case(name: str, **overrides) -> PagedCase:
+    spec = dict(WORKLOADS[name])
+    spec.update(overrides)
+    kind = spec.pop("kind")
+    if kind == "decode":
+        spec.setdefault("kv_dtype", KV_E4M3)
+        return decode_case(**spec)
+    return sparse_prefill_case(**spec)

@@ -1,0 +1,212 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle for paged grouped-query attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header, table or constant with the
+ * GPU library: every value below is derived here from the format definitions.
+ *
+ * What it computes (sources, by page title and section):
+ *   - "[Kernel][SM70] Scale NVFP4 E4M3 decode batches", Purpose: FP8-E4M3,
+ *     GQA-6, D256 paged decode for batches of sequences, K/V read through a
+ *     page table.
+ *   - "[Kernel][SM70] Accelerate Qwen3.8 QSA paged prefill", Changes: each
+ *     query row attends to a selected token set exposed as a virtual page-4
+ *     table (the same paged attention with rows in place of sequences), with
+ *     contiguous or interleaved K/V strides and rows clamped to their live
+ *     length; invalid (empty) rows are inert.
+ * The method reaches an exact result (softmax attention), so the oracle is
+ * that definition written out:
+ *   1. decode every input exactly (IEEE binary16 for q and FP16 KV, the OCP
+ *      E4M3FN definition for FP8 KV; real value = per-tensor scale * code),
+ *   2. de-page the sequence's K and V into contiguous fp64 rows,
+ *   3. z_t = sm_scale * <q_h, K_t>,  w_t = exp(z_t - max z),
+ *      o_h = sum_t w_t V_t / sum_t w_t,  and o_h = 0 for an empty sequence.
+ * No blocking, fusion or reordering beyond that.  Parallelism: one OpenMP
+ * task per (sequence, kv head) pair; each pair is computed serially.
+ *
+ * Every function here is pinned by the CPU test suite (closed forms,
+ * invariants, and library routines: torch's float8_e4m3fn cast, numpy's
+ * binary16 decode, torch scaled_dot_product_attention in float64).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Error codes returned by oracle_paged_gqa. */
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG (-1)      /* bad sizes / null pointers                 */
+#define ORACLE_ERR_PAGE (-2)     /* a page id outside [0, num_pages)          */
+#define ORACLE_ERR_TABLE (-3)    /* a length needs more pages than the table  */
+#define ORACLE_ERR_NOMEM (-4)
+
+/* OCP 8-bit floating point, E4M3FN variant (bias 7, no infinities, the two
+ * codes S.1111.111 are NaN, largest finite magnitude 448).  The pages name
+ * the KV format "FP8-E4M3"; this is the variant whose maximum is 448. */
+double oracle_e4m3_value(uint8_t code) {
+  int s = code >> 7;
+  int e = (code >> 3) & 15;
+  int m = code & 7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m, -9);               /* subnormal: m/8 * 2^(1-7) */
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, e - 7);  /* normal */
+  return s ? -mag : mag;
+}
+
+/* IEEE 754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double oracle_f16_value(uint16_t bits) {
+  int s = bits >> 15;
+  int e = (bits >> 10) & 31;
+  int m = bits & 1023;
+  double mag;
+  if (e == 31) {
+    if (m != 0) return NAN;
+    mag = INFINITY;
+  } else if (e == 0) {
+    mag = ldexp((double)m, -24);
+  } else {
+    mag = ldexp(1.0 + (double)m / 1024.0, e - 15);
+  }
+  return s ? -mag : mag;
+}
+
+void oracle_e4m3_table(double* out256) {
+  for (int c = 0; c < 256; ++c) out256[c] = oracle_e4m3_value((uint8_t)c);
+}
+
+void oracle_f16_decode(const uint16_t* in, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_value(in[i]);
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Read one KV element as a real number.  kv_dtype 0 = FP16 (scale ignored),
+ * 1 = FP8-E4M3 (real value = scale * decoded code). */
+static double kv_element(const uint8_t* base, int64_t elem_index, int kv_dtype,
+                         double scale) {
+  if (kv_dtype == 0) {
+    uint16_t bits;
+    memcpy(&bits, base + 2 * elem_index, 2);
+    return oracle_f16_value(bits);
+  }
+  return scale * oracle_e4m3_value(base[elem_index]);
+}
+
+/*
+ * Paged GQA attention for a subset of sequences (decode) or query rows
+ * (sparse prefill, where each row's "sequence" is its virtual page table).
+ *
+ * q        : fp16 bits, [n_seq][Hq][D], contiguous.
+ * k_base, v_base : host byte pointers to element (page 0, slot 0, head 0,
+ *            dim 0) of the K and V pools.  Element (p, t, g, d) sits at
+ *            element offset p*page_stride + t*token_stride + g*head_stride + d.
+ * table    : int32 [n_seq][max_pages]; logical token i of sequence b lives in
+ *            physical page table[b][i / page_size], slot i % page_size.
+ * lens     : int32 [n_seq]; length <= 0 means an empty (inert) sequence.
+ * seq_ids  : which sequences to compute (n_ids of them); NULL = all n_seq.
+ * out      : fp64 [n_ids][Hq][D].
+ */
+int oracle_paged_gqa(const uint16_t* q, int32_t n_seq, int32_t Hq, int32_t Hkv,
+                     int32_t D, const uint8_t* k_base, const uint8_t* v_base,
+                     int64_t page_stride, int64_t token_stride,
+                     int64_t head_stride, int32_t num_pages, int32_t page_size,
+                     int32_t kv_dtype, double k_scale, double v_scale,
+                     const int32_t* table, int32_t max_pages,
+                     const int32_t* lens, double sm_scale,
+                     const int32_t* seq_ids, int32_t n_ids, double* out) {
+  if (!q || !k_base || !v_base || !table || !lens || !out) return ORACLE_ERR_ARG;
+  if (n_seq < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 ||
+      page_size <= 0 || num_pages < 0 || max_pages < 0 ||
+      (kv_dtype != 0 && kv_dtype != 1))
+    return ORACLE_ERR_ARG;
+  if (!seq_ids) n_ids = n_seq;
+  const int32_t group = Hq / Hkv;
+
+  /* Validate every table entry that will be read before computing. */
+  for (int32_t i = 0; i < n_ids; ++i) {
+    int32_t b = seq_ids ? seq_ids[i] : i;
+    if (b < 0 || b >= n_seq) return ORACLE_ERR_ARG;
+    int32_t L = lens[b];
+    if (L <= 0) continue;
+    int64_t pages_needed = ((int64_t)L + page_size - 1) / page_size;
+    if (pages_needed > max_pages) return ORACLE_ERR_TABLE;
+    for (int64_t j = 0; j < pages_needed; ++j) {
+      int32_t p = table[(int64_t)b * max_pages + j];
+      if (p < 0 || p >= num_pages) return ORACLE_ERR_PAGE;
+    }
+  }
+
+  int failed = 0;
+  int64_t n_items = (int64_t)n_ids * Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t item = 0; item < n_items; ++item) {
+    int32_t i = (int32_t)(item / Hkv);
+    int32_t g = (int32_t)(item % Hkv);
+    int32_t b = seq_ids ? seq_ids[i] : i;
+    int32_t L = lens[b];
+    double* o_group = out + ((int64_t)i * Hq + (int64_t)g * group) * D;
+    if (L <= 0) {
+      memset(o_group, 0, sizeof(double) * (size_t)group * D);
+      continue;
+    }
+    /* Step 2: de-page this sequence's K and V rows for kv head g. */
+    double* Kd = (double*)malloc(sizeof(double) * (size_t)L * D);
+    double* Vd = (double*)malloc(sizeof(double) * (size_t)L * D);
+    double* z = (double*)malloc(sizeof(double) * (size_t)L);
+    double* qd = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!Kd || !Vd || !z || !qd) {
+      free(Kd); free(Vd); free(z); free(qd);
+#pragma omp atomic write
+      failed = 1;
+      continue;
+    }
+    for (int32_t t = 0; t < L; ++t) {
+      int64_t page = table[(int64_t)b * max_pages + t / page_size];
+      int64_t slot = t % page_size;
+      int64_t row = page * page_stride + slot * token_stride + (int64_t)g * head_stride;
+      for (int32_t d = 0; d < D; ++d) {
+        Kd[(int64_t)t * D + d] = kv_element(k_base, row + d, kv_dtype, k_scale);
+        Vd[(int64_t)t * D + d] = kv_element(v_base, row + d, kv_dtype, v_scale);
+      }
+    }
+    /* Step 3: softmax attention for every query head of the group. */
+    for (int32_t hh = 0; hh < group; ++hh) {
+      int32_t h = g * group + hh;
+      const uint16_t* qrow = q + ((int64_t)b * Hq + h) * D;
+      for (int32_t d = 0; d < D; ++d) qd[d] = oracle_f16_value(qrow[d]);
+      double zmax = -INFINITY;
+      for (int32_t t = 0; t < L; ++t) {
+        double acc = 0.0;
+        for (int32_t d = 0; d < D; ++d) acc += qd[d] * Kd[(int64_t)t * D + d];
+        z[t] = sm_scale * acc;
+        if (z[t] > zmax) zmax = z[t];
+      }
+      double wsum = 0.0;
+      for (int32_t t = 0; t < L; ++t) {
+        z[t] = exp(z[t] - zmax); /* z now holds the unnormalised weight */
+        wsum += z[t];
+      }
+      double* o = o_group + (int64_t)hh * D;
+      for (int32_t d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int32_t t = 0; t < L; ++t) acc += z[t] * Vd[(int64_t)t * D + d];
+        o[d] = acc / wsum;
+      }
+    }
+    free(Kd); free(Vd); free(z); free(qd);
+  }
+  return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}

@@ -1,0 +1,323 @@
+"""Checks that pin the fp64 oracle to facts other than itself.
+
+Each ``pin_*`` function takes the path of an oracle library build and raises
+AssertionError when the oracle disagrees with:
+  - a library routine that implements the same definition independently
+    (torch's float8_e4m3fn cast, numpy's binary16 decode, torch's
+    scaled_dot_product_attention in float64 with a boolean mask for the
+    selected-token case),
+  - a closed form (context length 1, uniform keys, zero query, two tokens,
+    one dominating key),
+  - an invariant of the definition (physical page permutation, K/V layout,
+    logical token order, scale factoring, linearity in the V scale),
+  - the E4M3 spot values worked out from the format definition
+    (tests/golden/e4m3_spot_values.txt).
+The same functions run against deliberately broken oracle builds in
+test_oracle_mutants.py, which shows that each planted mistake fails a pin.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from fp8_kv_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------- helpers
+def logical_kv(case: inputs.PagedCase, b: int):
+    """K, V of sequence b as float64 [L][Hkv][D] for an identity-table,
+    contiguous-layout case (pages b*max_pages.. in order: a plain reshape)."""
+    assert case.layout == "contiguous"
+    mp = case.table.shape[1]
+    assert np.array_equal(case.table[b], np.arange(b * mp, (b + 1) * mp))
+    L = int(case.lens[b])
+    P, hkv, d = case.page_size, case.num_kv_heads, case.head_dim
+    ks = case.k_store.reshape(case.num_pages, P, hkv, d)[b * mp:(b + 1) * mp]
+    vs = case.v_store.reshape(case.num_pages, P, hkv, d)[b * mp:(b + 1) * mp]
+    ks = ks.reshape(mp * P, hkv, d)[:L]
+    vs = vs.reshape(mp * P, hkv, d)[:L]
+    return decode_kv(ks, case.kv_dtype, case.k_scale), decode_kv(vs, case.kv_dtype, case.v_scale)
+
+
+def decode_kv(arr: np.ndarray, kv_dtype: int, scale: float) -> np.ndarray:
+    """Library decode of pool values: numpy binary16, torch float8_e4m3fn."""
+    if kv_dtype == inputs.KV_FP16:
+        return arr.astype(np.float64)
+    t = torch.from_numpy(np.ascontiguousarray(arr)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy() * scale
+
+
+def sdpa(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float,
+         mask: np.ndarray | None = None) -> np.ndarray:
+    """torch scaled_dot_product_attention in float64 on the CPU.
+    q [Hq][D]; k, v [L][Hkv][D]; returns [Hq][D]."""
+    tq = torch.from_numpy(q.astype(np.float64))[None, :, None, :]
+    tk = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))[None]
+    tv = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))[None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None, None, :]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=m, scale=sm_scale, enable_gqa=True)
+    return o[0, :, 0, :].numpy()
+
+
+def run(case: inputs.PagedCase, lib: str, **kw) -> np.ndarray:
+    return oracle.paged_gqa(**case.oracle_kwargs(), lib_path=lib, **kw)
+
+
+def close(a, b, rtol=1e-12, atol=1e-13, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    err = np.abs(a - b)
+    bound = atol + rtol * np.abs(b)
+    assert np.all(err <= bound), f"{what}: max err {err.max():.3e}"
+
+
+def _with_kv(case: inputs.PagedCase, kfun=None, vfun=None) -> inputs.PagedCase:
+    """Copy of a contiguous case with K and/or V storage rewritten."""
+    import dataclasses
+    ks = case.k_store.copy() if kfun is None else kfun(case.k_store.copy())
+    vs = case.v_store.copy() if vfun is None else vfun(case.v_store.copy())
+    return dataclasses.replace(case, k_store=ks, v_store=vs)
+
+
+# -------------------------------------------------------------- the pins
+def pin_e4m3_vs_torch(lib: str) -> None:
+    """All 256 codes against torch's float8_e4m3fn -> float64 (NaN == NaN)."""
+    ours = oracle.e4m3_table(lib)
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(
+        torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.flatnonzero(np.isnan(ours)).tolist() == [0x7F, 0xFF]
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.array_equal(np.signbit(ours[fin]), np.signbit(ref[fin]))
+    assert np.nanmax(ours) == 448.0 and np.nanmin(ours) == -448.0
+
+
+def pin_e4m3_golden(lib: str) -> None:
+    ours = oracle.e4m3_table(lib)
+    n = 0
+    with open(os.path.join(GOLDEN, "e4m3_spot_values.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            code_s, val_s = line.split()[:2]
+            code, val = int(code_s, 16), float(val_s)
+            if math.isnan(val):
+                assert math.isnan(ours[code]), hex(code)
+            else:
+                assert ours[code] == val and math.copysign(1, ours[code]) == math.copysign(1, val), hex(code)
+            n += 1
+    assert n >= 15
+
+
+def pin_f16_vs_numpy(lib: str) -> None:
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.f16_decode(bits, lib)
+    ref = bits.view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.array_equal(np.signbit(ours[fin]), np.signbit(ref[fin]))
+
+
+def pin_sdpa(lib: str) -> None:
+    """Identity tables, contiguous layout: the paged result equals torch's
+    float64 attention on the logical K/V (GQA groups of consecutive heads)."""
+    cases = [
+        dict(batch=3, lens=[37, 16, 50], page_size=16, kv_dtype=inputs.KV_FP16),
+        dict(batch=2, lens=[64, 29], page_size=8, kv_dtype=inputs.KV_E4M3, scales=(0.75, 1.5)),
+        dict(batch=2, lens=[33, 7], page_size=4, kv_dtype=inputs.KV_E4M3, scales="uniform",
+             num_q_heads=12, num_kv_heads=2),
+        dict(batch=1, lens=[20], page_size=5, kv_dtype=inputs.KV_FP16, num_q_heads=8,
+             num_kv_heads=4, head_dim=64),
+    ]
+    for i, kw in enumerate(cases):
+        case = inputs.decode_case(table="identity", seed=100 + i, **kw)
+        got = run(case, lib)
+        for b in range(case.n):
+            k, v = logical_kv(case, b)
+            ref = sdpa(case.q[b].astype(np.float64), k, v, case.sm_scale)
+            close(got[b], ref, rtol=1e-11, atol=1e-13, what=f"sdpa case {i} seq {b}")
+
+
+def pin_sparse_vs_masked_sdpa(lib: str) -> None:
+    """Sparse prefill: each row equals dense attention over the whole (tiny)
+    pool, masked to exactly the tokens its virtual page-4 table selects.  Tail
+    counts 1, 2, 3 and 0."""
+    for tail in (1, 2, 3, 0):
+        case = inputs.sparse_prefill_case(rows=5, selected_blocks=6, tail=tail, pool_blocks=16,
+                                          layout="contiguous", seed=7 + tail,
+                                          kv_dtype=inputs.KV_E4M3, scales="uniform")
+        got = run(case, lib)
+        P, hkv, d = 4, case.num_kv_heads, case.head_dim
+        kall = decode_kv(case.k_store.reshape(-1, hkv, d), case.kv_dtype, case.k_scale)
+        vall = decode_kv(case.v_store.reshape(-1, hkv, d), case.kv_dtype, case.v_scale)
+        for r in range(case.n):
+            mask = np.zeros(kall.shape[0], dtype=bool)
+            nsel = case.meta["selected_blocks"]
+            for blk in case.table[r, :nsel]:
+                mask[P * blk:P * blk + P] = True
+            if tail:
+                c = case.table[r, nsel]
+                mask[P * c:P * c + tail] = True
+            assert mask.sum() == case.lens[r]
+            ref = sdpa(case.q[r].astype(np.float64), kall, vall, case.sm_scale, mask)
+            close(got[r], ref, rtol=1e-11, atol=1e-13, what=f"tail {tail} row {r}")
+
+
+def pin_closed_forms(lib: str) -> None:
+    base = inputs.decode_case(batch=1, lens=1, page_size=4, kv_dtype=inputs.KV_E4M3,
+                              table="identity", scales=(1.25, 0.625), seed=3)
+    # Context length 1: output = V_0 (times the V scale), exactly.
+    got = run(base, lib)
+    v0 = decode_kv(base.v_store.reshape(-1, 1, 256)[0], base.kv_dtype, base.v_scale)
+    for h in range(6):
+        assert np.array_equal(got[0, h], v0[0]), "L=1"
+
+    # Uniform keys (every K row identical): output = mean of V.
+    L = 23
+    case = inputs.decode_case(batch=1, lens=L, page_size=4, kv_dtype=inputs.KV_E4M3,
+                              table="identity", scales=(1.5, 0.75), seed=4)
+
+    def same_rows(ks):
+        ks = ks.reshape(-1, 256)
+        ks[:] = ks[0]
+        return ks.reshape(case.k_store.shape)
+    uni = _with_kv(case, kfun=same_rows)
+    got = run(uni, lib)
+    _, v = logical_kv(uni, 0)
+    for h in range(6):
+        close(got[0, h], v[:, 0].mean(axis=0), rtol=1e-13, atol=1e-15, what="uniform keys")
+
+    # Zero query: output = mean of V whatever the keys.
+    import dataclasses
+    zq = dataclasses.replace(case, q=np.zeros_like(case.q))
+    got = run(zq, lib)
+    _, v = logical_kv(zq, 0)
+    close(got[0, 0], v[:, 0].mean(axis=0), rtol=1e-13, atol=1e-15, what="zero q")
+
+    # Two tokens: o = s*V1 + (1-s)*V0, s = sigmoid(z1 - z0), K0 = 0, K1 = e_0.
+    two = inputs.decode_case(batch=1, lens=2, page_size=2, kv_dtype=inputs.KV_E4M3,
+                             table="identity", scales=(1.75, 1.25), seed=5, sm_scale=0.3)
+
+    def keys(ks):
+        ks = ks.reshape(-1, 256)
+        ks[:] = 0
+        ks[1, 0] = 0x38  # 1.0
+        return ks.reshape(two.k_store.shape)
+    two = _with_kv(two, kfun=keys)
+    qv = np.zeros_like(two.q)
+    qv[0, :, 0] = np.array([1.0, -2.0, 3.5, 0.0, 0.5, -0.25], dtype=np.float16)
+    two = dataclasses.replace(two, q=qv)
+    got = run(two, lib)
+    _, v = logical_kv(two, 0)
+    for h in range(6):
+        dz = 0.3 * 1.75 * float(qv[0, h, 0])
+        s = 1.0 / (1.0 + math.exp(-dz))
+        close(got[0, h], s * v[1, 0] + (1 - s) * v[0, 0], rtol=1e-13, atol=1e-15,
+              what=f"two tokens h{h}")
+
+    # One key dominating by a logit gap >= 40: output = that key's V to e^-40.
+    dom = inputs.decode_case(batch=1, lens=9, page_size=4, kv_dtype=inputs.KV_FP16,
+                             table="identity", seed=6, sm_scale=1.0)
+
+    def domkeys(ks):
+        ks = ks.reshape(-1, 256)
+        ks[:] = 0
+        ks[5, 3] = 64.0
+        return ks.reshape(dom.k_store.shape)
+    dom = _with_kv(dom, kfun=domkeys)
+    qd = np.zeros_like(dom.q)
+    qd[0, :, 3] = 1.0
+    dom = dataclasses.replace(dom, q=qd)
+    got = run(dom, lib)
+    _, v = logical_kv(dom, 0)
+    close(got[0, 0], v[5, 0], rtol=1e-15, atol=1e-16 + 9 * math.exp(-64) * np.abs(v).max(),
+          what="dominant key")
+
+
+def pin_invariants(lib: str) -> None:
+    import dataclasses
+    case = inputs.decode_case(batch=3, lens=[45, 64, 17], page_size=8, kv_dtype=inputs.KV_E4M3,
+                              scales=(0.8, 1.7), seed=11)
+    ref = run(case, lib)
+
+    # Physical page permutation with the table remapped: bitwise identical.
+    rng = np.random.default_rng(12)
+    perm = rng.permutation(case.num_pages)           # page p moves to perm[p]
+    ks = np.empty_like(case.k_store)
+    vs = np.empty_like(case.v_store)
+    ks[perm] = case.k_store
+    vs[perm] = case.v_store
+    moved = dataclasses.replace(case, k_store=ks, v_store=vs,
+                                table=perm[case.table].astype(np.int32))
+    assert np.array_equal(run(moved, lib), ref), "page permutation"
+
+    # K/V layout: contiguous, interleaved and head-major give identical results.
+    for layout in ("interleaved", "head_major"):
+        other = inputs.decode_case(batch=3, lens=[45, 64, 17], page_size=8,
+                                   kv_dtype=inputs.KV_E4M3, scales=(0.8, 1.7), seed=11,
+                                   layout=layout)
+        assert np.array_equal(run(other, lib), ref), layout
+
+    # Scale factoring: (k_scale * c, sm_scale / c) leaves the logits unchanged.
+    f = dataclasses.replace(case, k_scale=case.k_scale * 4.0, sm_scale=case.sm_scale / 4.0)
+    close(run(f, lib), ref, rtol=1e-12, atol=1e-14, what="scale factoring")
+
+    # Linearity in the V scale (a power of two: exact).
+    lin = dataclasses.replace(case, v_scale=case.v_scale * 2.0)
+    assert np.array_equal(run(lin, lib), 2.0 * ref), "v scale"
+
+    # Logical token order: permuting the full pages a sequence lists (a
+    # length that is a multiple of the page size) changes only rounding.
+    b = 1
+    t2 = case.table.copy()
+    t2[b, :8] = t2[b, :8][rng.permutation(8)]
+    shuf = dataclasses.replace(case, table=t2)
+    close(run(shuf, lib)[b], ref[b], rtol=1e-12, atol=1e-14, what="token order")
+
+    # Table entries past ceil(L / P) are never read.
+    t3 = case.table.copy()
+    for i, L in enumerate(case.lens):
+        t3[i, -(-int(L) // 8):] = -12345
+    assert np.array_equal(run(dataclasses.replace(case, table=t3), lib), ref), "unread entries"
+
+    # Empty sequences are inert: zeros, and their table is not read.
+    e = dataclasses.replace(case, lens=np.array([0, 64, -3], dtype=np.int32),
+                            table=np.where(np.arange(3)[:, None] == 1, case.table, -1).astype(np.int32))
+    got = run(e, lib)
+    assert np.all(got[0] == 0) and np.all(got[2] == 0)
+    assert np.array_equal(got[1], ref[1])
+
+    # Subset evaluation equals the full evaluation.
+    assert np.array_equal(run(case, lib, seq_ids=[2, 0]), ref[[2, 0]])
+
+
+def pin_errors(lib: str) -> None:
+    import dataclasses
+    case = inputs.decode_case(batch=2, lens=[10, 12], page_size=4, kv_dtype=inputs.KV_FP16,
+                              seed=13)
+    bad = case.table.copy()
+    bad[1, 2] = case.num_pages
+    try:
+        run(dataclasses.replace(case, table=bad), lib)
+        raise AssertionError("out-of-range page id accepted")
+    except oracle.OracleError as e:
+        assert e.code == oracle.ORACLE_ERR_PAGE
+    try:
+        run(dataclasses.replace(case, lens=np.array([10, 13], dtype=np.int32)), lib)
+        raise AssertionError("over-long sequence accepted")
+    except oracle.OracleError as e:
+        assert e.code == oracle.ORACLE_ERR_TABLE
+
+
+ALL_PINS = [pin_e4m3_vs_torch, pin_e4m3_golden, pin_f16_vs_numpy, pin_sdpa,
+            pin_sparse_vs_masked_sdpa, pin_closed_forms, pin_invariants, pin_errors]

@@ -1,0 +1,74 @@
+"""Plant plausible mistakes in a copy of the oracle and show a pin catches each.
+
+Each mutant is a one-token edit of oracle.c (a dropped term, a wrong sign,
+index or bias, a transposed operand), compiled on the CPU into a temporary
+library.  The real oracle is untouched.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "drop_sm_scale": ("z[t] = sm_scale * acc;", "z[t] = acc;"),
+    "exp_sign": ("z[t] = exp(z[t] - zmax);", "z[t] = exp(zmax - z[t]);"),
+    "no_normalise": ("o[d] = acc / wsum;", "o[d] = acc;"),
+    "page_slot_swapped": ("table[(int64_t)b * max_pages + t / page_size]",
+                          "table[(int64_t)b * max_pages + t % page_size]"),
+    "slot_dropped": ("int64_t slot = t % page_size;", "int64_t slot = 0;"),
+    "head_mapping": ("int32_t h = g * group + hh;", "int32_t h = hh * Hkv + g;"),
+    "kv_head_ignored": ("+ (int64_t)g * head_stride;", ";"),
+    "e4m3_bias": ("mag = ldexp(1.0 + (double)m / 8.0, e - 7);",
+                  "mag = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "e4m3_subnormal": ("mag = ldexp((double)m, -9);", "mag = ldexp((double)m, -10);"),
+    "e4m3_nan": ("if (e == 15 && m == 7) return NAN;", "if (e == 15 && m == 7) return 480.0;"),
+    "f16_bias": ("mag = ldexp(1.0 + (double)m / 1024.0, e - 15);",
+                 "mag = ldexp(1.0 + (double)m / 1024.0, e - 14);"),
+    "v_scale_dropped": ("Vd[(int64_t)t * D + d] = kv_element(v_base, row + d, kv_dtype, v_scale);",
+                        "Vd[(int64_t)t * D + d] = kv_element(v_base, row + d, kv_dtype, 1.0);"),
+    "k_scale_dropped": ("Kd[(int64_t)t * D + d] = kv_element(k_base, row + d, kv_dtype, k_scale);",
+                        "Kd[(int64_t)t * D + d] = kv_element(k_base, row + d, kv_dtype, 1.0);"),
+    "k_v_swapped": ("Kd[(int64_t)t * D + d] = kv_element(k_base,",
+                    "Kd[(int64_t)t * D + d] = kv_element(v_base,"),
+    "last_token_dropped": ("for (int32_t t = 0; t < L; ++t) {\n      int64_t page",
+                           "for (int32_t t = 0; t < L - 1; ++t) {\n      int64_t page"),
+    "empty_not_inert": ("if (L <= 0) {\n      memset", "if (L < 0) {\n      memset"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation site for {name} not unique"
+    src = tmp_path / "oracle_mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = str(tmp_path / "liboracle_mutant.so")
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
+                    "-ffp-contract=off", str(src), "-o", lib, "-lm"], check=True)
+    # Run the pins in a child process: a mutant may also crash outright,
+    # which counts as caught.
+    script = (
+        "import sys\n"
+        "from tests import oracle_pins\n"
+        "failed = []\n"
+        "for pin in oracle_pins.ALL_PINS:\n"
+        "    try:\n"
+        "        pin(sys.argv[1])\n"
+        "    except Exception as e:\n"
+        "        failed.append(pin.__name__)\n"
+        "print('FAILED_PINS', failed)\n")
+    res = subprocess.run([sys.executable, "-c", script, lib], cwd=ROOT,
+                         capture_output=True, text=True, timeout=600)
+    crashed = res.returncode < 0          # killed by a signal (e.g. SIGSEGV)
+    failed_some = "FAILED_PINS [" in res.stdout and "FAILED_PINS []" not in res.stdout
+    assert crashed or failed_some, (
+        f"mutant {name} not caught: rc={res.returncode}\n{res.stdout}\n{res.stderr[-2000:]}")
+    print(name, "crashed" if crashed else res.stdout.strip())
