@@ -1,0 +1,174 @@
+#!/usr/bin/env python3
+"""Benchmark: paged GQA decode, B=16 x 16K context, FP8-E4M3 KV, page 128.
+
+One step = one paged_gqa_decode call over the whole batch (every stage of the
+path: page-table gather, E4M3 dequant, QK^T, online softmax, PV, split
+merge).  Inputs are resident in HBM before timing starts.  The KV pool is
+replicated into R separate device copies and the steps rotate through them,
+so consecutive calls cannot be served from the 256 MB last-level cache.
+
+Prints ONE JSON line.  `value` is KV-read GB/s: algorithmic KV bytes per call
+(every live token's K and V row read once) divided by the average call time
+measured with HIP events on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("KV-read HBM GB/s (% of peak) and µs/call, paged GQA decode B16×16K E4M3")
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_b16_16k_e4m3_p128.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "fp8_kv_amd", "csrc", f)
+                  for f in ("pgqa_kernels.hip", "pgqa_api.hip", "pgqa_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != src_hash:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float) -> dict:
+    """The fp64 oracle, as it is, on the host cores: repeat whole calls on
+    the same workload until about `budget_s` seconds have passed."""
+    import oracle
+
+    n_calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.paged_gqa(**case.oracle_kwargs())
+        n_calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n_calls >= 50:
+            break
+    per_call = el / n_calls
+    return {"value": round(case.kv_bytes_read() / per_call / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n_calls} whole calls of the same workload, {per_call * 1e3:.1f} ms each"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="decode_b16_16k_e4m3_p128")
+    ap.add_argument("--pools", type=int, default=8,
+                    help="device copies of the KV pool rotated between steps (1 = warm cache)")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from fp8_kv_amd import inputs, pgqa
+
+    pgqa.load()
+    torch.cuda.set_device(0)
+    case = inputs.workload_case(args.workload)
+    prefill = args.workload.startswith("prefill")
+    q, pool0, table, lens = pgqa.device_case(case)
+    n, hq, _ = q.shape
+    R = max(1, args.pools)
+    pools = [pool0]
+    for _ in range(R - 1):
+        ks = pool0.storage[0].clone()
+        vs = ks if pool0.storage[1] is pool0.storage[0] else pool0.storage[1].clone()
+        kflat, vflat = ks.reshape(-1), vs.reshape(-1)
+        pools.append(pgqa.KVPool(kflat[case.k_offset:], vflat[case.v_offset:], case.page_stride,
+                                 case.token_stride, case.head_stride, case.num_pages,
+                                 case.page_size, case.kv_dtype, case.k_scale, case.v_scale,
+                                 storage=(ks, vs)))
+    out = torch.empty_like(q)
+    splits = pgqa.paged_gqa_num_splits(n, case.num_kv_heads, case.max_seq_len, args.num_splits)
+    wsb = pgqa.paged_gqa_workspace_bytes(n, hq, case.num_kv_heads, case.max_seq_len,
+                                         args.num_splits)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    fn = pgqa.paged_gqa_prefill_sparse if prefill else pgqa.paged_gqa_decode
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        fn(q, pools[i % R], table, lens, case.max_seq_len, case.sm_scale, out,
+           num_kv_heads=case.num_kv_heads, workspace=ws, num_splits=args.num_splits,
+           stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    elapsed_ms = start.elapsed_time(end)
+    ms = elapsed_ms / args.steps
+    kv_bytes = case.kv_bytes_read()
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+
+    src_hash = kernel_source_hash()
+    traffic = measured_traffic(src_hash)
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 kv -> f16 mfma, f32 accumulate" if case.kv_dtype == inputs.KV_E4M3
+                 else "f16 kv -> f16 mfma, f32 accumulate",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "batch_or_rows": n, "q_heads": hq,
+            "kv_heads": case.num_kv_heads, "head_dim": 256,
+            "context": int(case.max_seq_len), "page_size": case.page_size,
+            "kv_dtype": "fp8_e4m3" if case.kv_dtype == inputs.KV_E4M3 else "fp16",
+            "layout": case.layout, "num_splits": splits, "pools_rotated": R,
+            "us_per_call": round(ms * 1e3, 3), "kv_bytes_per_call": kv_bytes,
+            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "kernel_source_hash": src_hash,
+        },
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

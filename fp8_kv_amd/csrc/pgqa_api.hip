@@ -1,0 +1,233 @@
+// C-ABI host layer of libpgqa: argument validation, split planning and
+// launches on the caller's stream.  Declared in include/pgqa.h.
+//
+// Validation runs before any HIP call, so every argument error is reported
+// without touching a device ("fail closed": nothing launched, nothing
+// written).  The only HIP queries are the current device and its compute
+// unit count (cached per device), needed for the automatic split count.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "pgqa.h"
+#include "pgqa_internal.h"
+
+namespace {
+
+using pgqa::kChunkAlign;
+using pgqa::kHeadDim;
+using pgqa::kMaxGroup;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Compute units of the current device, or -1 if HIP cannot say.
+int current_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices) {
+    int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return -1;
+  if (dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+struct SplitPlan {
+  int32_t splits;
+  int32_t chunk;
+};
+
+// Key-range splits: aim for two resident workgroups per compute unit, never
+// fewer than kChunkAlign tokens (one tile per wave) per split.
+SplitPlan plan_splits(int64_t groups, int32_t max_len, int32_t requested, int cus) {
+  const int64_t len = max_len > 0 ? max_len : 1;
+  const int64_t max_splits = ceil_div(len, kChunkAlign);
+  int64_t s;
+  if (requested > 0) {
+    s = requested;
+  } else {
+    const int64_t target_wgs = 2LL * (cus > 0 ? cus : 256);
+    s = ceil_div(target_wgs, groups > 0 ? groups : 1);
+  }
+  if (s > max_splits) s = max_splits;
+  if (s < 1) s = 1;
+  const int64_t chunk = ceil_div(ceil_div(len, s), kChunkAlign) * kChunkAlign;
+  return SplitPlan{static_cast<int32_t>(ceil_div(len, chunk)), static_cast<int32_t>(chunk)};
+}
+
+// Checks that need no HIP call.  Returns PGQA_OK or an error code.
+int validate_sizes(int32_t n, int32_t hq, int32_t hkv, int32_t head_dim, int32_t max_len,
+                   int32_t num_splits) {
+  if (head_dim != kHeadDim) return PGQA_ERR_SHAPE;
+  if (n < 0 || hkv < 1 || hq < 1 || hq % hkv != 0) return PGQA_ERR_SHAPE;
+  const int32_t group = hq / hkv;
+  if (group > kMaxGroup) return PGQA_ERR_SHAPE;
+  if (max_len < 0 || max_len > PGQA_MAX_SEQ_LEN) return PGQA_ERR_SHAPE;
+  if (num_splits < 0) return PGQA_ERR_ARG;
+  // The grid is splits * n * hkv workgroups in one dimension.
+  const int64_t max_splits = ceil_div(max_len > 0 ? max_len : 1, kChunkAlign);
+  if (static_cast<int64_t>(n) * hkv * max_splits > INT32_MAX) return PGQA_ERR_SHAPE;
+  return PGQA_OK;
+}
+
+int validate_call(const void* q, const pgqa_kv_pool* kv, const int32_t* table,
+                  int32_t max_pages, const int32_t* lens, int32_t max_len, int32_t n,
+                  int32_t hq, int32_t hkv, int32_t head_dim, float sm_scale,
+                  int32_t num_splits, const void* out) {
+  int rc = validate_sizes(n, hq, hkv, head_dim, max_len, num_splits);
+  if (rc != PGQA_OK) return rc;
+  if (!kv) return PGQA_ERR_NULL;
+  if (kv->kv_dtype != PGQA_KV_FP16 && kv->kv_dtype != PGQA_KV_E4M3) return PGQA_ERR_DTYPE;
+  if (!std::isfinite(sm_scale)) return PGQA_ERR_ARG;
+  if (kv->kv_dtype == PGQA_KV_E4M3 && (!std::isfinite(kv->k_scale) || !std::isfinite(kv->v_scale)))
+    return PGQA_ERR_ARG;
+  if (n == 0) return PGQA_OK;
+  if (!q || !out || !table || !lens || !kv->k_base || !kv->v_base) return PGQA_ERR_NULL;
+  if (kv->page_size < 1 || kv->num_pages < 1 || max_pages < 1) return PGQA_ERR_SHAPE;
+  if (static_cast<int64_t>(max_len) > static_cast<int64_t>(max_pages) * kv->page_size)
+    return PGQA_ERR_SHAPE;
+  const int64_t es = kv->kv_dtype == PGQA_KV_FP16 ? 2 : 1;
+  if (kv->page_stride < 0 || kv->token_stride < 0 || kv->head_stride < 0) return PGQA_ERR_LAYOUT;
+  if ((kv->page_stride * es) % 16 || (kv->token_stride * es) % 16 || (kv->head_stride * es) % 16)
+    return PGQA_ERR_LAYOUT;
+  if (!aligned16(kv->k_base) || !aligned16(kv->v_base) || !aligned16(q) || !aligned16(out))
+    return PGQA_ERR_LAYOUT;
+  return PGQA_OK;
+}
+
+int run_attention(const void* q, const pgqa_kv_pool* kv, const int32_t* table, int32_t max_pages,
+                  const int32_t* lens, int32_t max_len, int32_t n, int32_t hq, int32_t hkv,
+                  int32_t head_dim, float sm_scale, int32_t num_splits, void* out,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_call(q, kv, table, max_pages, lens, max_len, n, hq, hkv, head_dim, sm_scale,
+                         num_splits, out);
+  if (rc != PGQA_OK || n == 0) return rc;
+
+  int cus = 0;
+  if (num_splits == 0) {
+    cus = current_cu_count();
+    if (cus <= 0) return PGQA_ERR_HIP;
+  }
+  const SplitPlan plan = plan_splits(static_cast<int64_t>(n) * hkv, max_len, num_splits, cus);
+  const size_t need =
+      plan.splits > 1 ? static_cast<size_t>(n) * hq * plan.splits * (kHeadDim + 1) * sizeof(float)
+                      : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return PGQA_ERR_WORKSPACE;
+
+  const bool fp8 = kv->kv_dtype == PGQA_KV_E4M3;
+  const int64_t es = fp8 ? 1 : 2;
+  pgqa::AttnParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_base = static_cast<const uint8_t*>(kv->k_base);
+  p.v_base = static_cast<const uint8_t*>(kv->v_base);
+  p.page_stride = kv->page_stride * es;
+  p.token_stride = kv->token_stride * es;
+  p.head_stride = kv->head_stride * es;
+  p.num_pages = kv->num_pages;
+  p.page_size = kv->page_size;
+  p.inv_page_size = 1.0f / static_cast<float>(kv->page_size);
+  p.table = table;
+  p.max_pages = max_pages;
+  p.lens = lens;
+  p.max_len = max_len;
+  p.n = n;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.group = hq / hkv;
+  const double log2e = 1.4426950408889634;
+  p.qk_scale_log2 =
+      static_cast<float>(static_cast<double>(sm_scale) * (fp8 ? kv->k_scale : 1.0) * log2e);
+  p.v_scale = fp8 ? kv->v_scale : 1.0f;
+  p.splits = plan.splits;
+  p.chunk = plan.chunk;
+  p.out = static_cast<uint16_t*>(out);
+  if (plan.splits > 1) {
+    p.ws_o = static_cast<float*>(workspace);
+    p.ws_lse = p.ws_o + static_cast<size_t>(n) * hq * plan.splits * kHeadDim;
+  }
+  hipError_t err = pgqa::launch_attention(p, fp8, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PGQA_OK : PGQA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t paged_gqa_num_splits(int32_t n, int32_t num_kv_heads, int32_t max_seq_len,
+                             int32_t num_splits) {
+  if (n < 0 || num_kv_heads < 1 || max_seq_len < 0 || max_seq_len > PGQA_MAX_SEQ_LEN ||
+      num_splits < 0)
+    return PGQA_ERR_ARG;
+  int cus = 0;
+  if (num_splits == 0) {
+    cus = current_cu_count();
+    if (cus <= 0) return PGQA_ERR_HIP;
+  }
+  return plan_splits(static_cast<int64_t>(n) * num_kv_heads, max_seq_len, num_splits, cus).splits;
+}
+
+size_t paged_gqa_workspace_bytes(int32_t n, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len, int32_t num_splits) {
+  if (validate_sizes(n, num_q_heads, num_kv_heads, head_dim, max_seq_len, num_splits) != PGQA_OK)
+    return SIZE_MAX;
+  const int32_t splits = paged_gqa_num_splits(n, num_kv_heads, max_seq_len, num_splits);
+  if (splits < 1) return SIZE_MAX;
+  if (splits == 1) return 0;
+  return static_cast<size_t>(n) * num_q_heads * splits * (kHeadDim + 1) * sizeof(float);
+}
+
+int paged_gqa_decode(const void* q, const pgqa_kv_pool* kv, const int32_t* page_table,
+                     int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len,
+                     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, float sm_scale, int32_t num_splits, void* out,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attention(q, kv, page_table, max_pages, seq_lens, max_seq_len, batch, num_q_heads,
+                       num_kv_heads, head_dim, sm_scale, num_splits, out, workspace,
+                       workspace_bytes, stream);
+}
+
+int paged_gqa_prefill_sparse(const void* q, const pgqa_kv_pool* kv, const int32_t* row_tables,
+                             int32_t max_pages, const int32_t* row_lens, int32_t max_row_len,
+                             int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, float sm_scale, int32_t num_splits, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attention(q, kv, row_tables, max_pages, row_lens, max_row_len, rows, num_q_heads,
+                       num_kv_heads, head_dim, sm_scale, num_splits, out, workspace,
+                       workspace_bytes, stream);
+}
+
+int e4m3_decode_table(float* out256, void* stream) {
+  if (!out256) return PGQA_ERR_NULL;
+  if (!aligned16(out256)) return PGQA_ERR_LAYOUT;
+  return pgqa::launch_e4m3_table(out256, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PGQA_OK
+             : PGQA_ERR_HIP;
+}
+
+const char* pgqa_error_string(int code) {
+  switch (code) {
+    case PGQA_OK: return "ok";
+    case PGQA_ERR_NULL: return "a required pointer is NULL";
+    case PGQA_ERR_SHAPE: return "unsupported or inconsistent sizes";
+    case PGQA_ERR_LAYOUT: return "pointer or stride not 16-byte aligned, or negative stride";
+    case PGQA_ERR_DTYPE: return "unknown kv_dtype";
+    case PGQA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case PGQA_ERR_HIP: return "HIP runtime error";
+    case PGQA_ERR_ARG: return "invalid scalar argument";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,471 @@
+// gfx950 kernels for paged grouped-query attention over an FP16 or FP8-E4M3
+// KV pool (decode batches and sparse prefill rows share the same kernel).
+//
+// Sources, by page title and section:
+//   "[Kernel][SM70] Scale NVFP4 E4M3 decode batches", Purpose: GQA-6, D256
+//     paged decode with FP8-E4M3 KV, paired (wide) KV loads, long-context
+//     routes.  Here: 16-byte loads that read whole K/V rows per instruction,
+//     and key-range splits merged by log-sum-exp for long contexts.
+//   "[Kernel][SM70] Accelerate Qwen3.8 QSA paged prefill", Changes: virtual
+//     page-4 tables, contiguous or interleaved strides without copies, rows
+//     clamped to their live length, invalid rows inert, page ids of a tile
+//     staged ahead of its loads.
+//
+// Work decomposition.  One workgroup of four waves owns one (sequence or row
+// b, kv head g, split s): the tokens [s*chunk, min((s+1)*chunk, L_b)).  Wave
+// w takes the 16-token tiles w, w+4, w+8, ... of that range and keeps its own
+// online-softmax state; the four states are merged through LDS at the end.
+// With one split the workgroup writes the fp16 output; with several it writes
+// a normalised fp32 partial and its log2-sum-exp, merged by combine_kernel.
+//
+// Per tile (lane = 16*qd + r, r = lane % 16, qd = lane / 16):
+//   QK^T on MFMA 16x16x32 f16: M = the 16 tokens (A = K rows, lane r holds
+//     token r), N = the query heads of the group padded to 16 (B = q^T, zero
+//     for heads >= group), K = head dim in 8 steps of 32.  The head dim is
+//     contracted in a permuted order that lets lane (r, qd) read four
+//     16-byte pieces of token r's row, so one load instruction covers whole
+//     64-byte runs of 16 rows.  Output: lane (r, qd) holds the logits of head
+//     r for tokens 4qd .. 4qd+3.
+//   Online softmax in the log2 domain on those 4 logits per lane; the row max
+//     needs only two cross-lane steps (lanes r, r+16, r+32, r+48).
+//   PV on MFMA 16x16x16 f16: M = 16 head-dim slots, N = heads, K = the 16
+//     tokens.  The probabilities are already in B-operand layout (lane (r,qd)
+//     = head r, tokens 4qd..4qd+3).  The A operand (V^T) wants 4 tokens of
+//     one dim per lane; lane (r, qd) loads 16 contiguous bytes of each of the
+//     tokens 4qd..4qd+3 (so one instruction reads 4 whole rows) and the 16
+//     MFMAs take the dims of those bytes in turn; a byte permute per pair of
+//     tokens builds each operand.  Output dim d of MFMA j, slot m is
+//     16*m + j (FP8) or 128*(j/8) + 8*m + j%8 (FP16).
+#include "pgqa_internal.h"
+
+namespace pgqa {
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the merge buffer
+
+// ------------------------------------------------------------ E4M3 decode
+// Two E4M3 codes (bytes 2*HI, 2*HI+1 of w) to two fp16 values.  Every E4M3
+// value is exactly a binary16 value, so with a unit scale this is exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+// Eight codes (bytes 8*HALF .. 8*HALF+7 of a 16-byte chunk) to an MFMA operand.
+template <int HALF>
+__device__ __forceinline__ h8_t e4m3x8_to_h8(u4_t c) {
+  u4_t r;
+  r[0] = e4m3x2_to_f16x2<false>(c[2 * HALF]);
+  r[1] = e4m3x2_to_f16x2<true>(c[2 * HALF]);
+  r[2] = e4m3x2_to_f16x2<false>(c[2 * HALF + 1]);
+  r[3] = e4m3x2_to_f16x2<true>(c[2 * HALF + 1]);
+  return __builtin_bit_cast(h8_t, r);
+}
+
+// (b.lo16, a.lo16) and (b.hi16, a.hi16) as one dword.
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(a, b, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(a, b, 0x07060302u);
+}
+
+__device__ __forceinline__ u4_t load16(const uint8_t* ptr) {
+  return *reinterpret_cast<const u4_t*>(ptr);
+}
+
+__device__ __forceinline__ uint16_t f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+// t / P and t % P for 0 <= t < 2^22 via a float reciprocal and one
+// branch-free correction (the float quotient is off by at most one).
+__device__ __forceinline__ int div_page(int t, int P, float invP, int& slot) {
+  int qt = static_cast<int>(static_cast<float>(t) * invP);
+  int rem = t - qt * P;
+  const int adj = rem < 0 ? -1 : (rem >= P ? 1 : 0);
+  qt += adj;
+  slot = rem - adj * P;
+  return qt;
+}
+
+template <bool FP8>
+struct Geo;
+template <>
+struct Geo<true> {
+  static constexpr int kK = 4;  // 16-byte K pieces per lane per tile
+  static constexpr int kV = 1;  // 16-byte V pieces per lane per token
+};
+template <>
+struct Geo<false> {
+  static constexpr int kK = 8;
+  static constexpr int kV = 2;
+};
+
+template <bool FP8>
+struct TileRegs {
+  u4_t k[Geo<FP8>::kK];
+  u4_t v[4][Geo<FP8>::kV];
+};
+
+template <bool FP8>
+struct Wave {
+  // constant per wave
+  const AttnParams& p;
+  const int32_t* tab;
+  int64_t head_off;  // g * head_stride (bytes)
+  int s0, s1, wave, r, qd;
+  h8_t qop[8];
+  // running state
+  f4_t acc[16];
+  float m_run, l_run;
+  bool bad;
+
+  __device__ __forceinline__ int tile_start(int k) const {
+    return s0 + (wave + kWaves * k) * kTile;
+  }
+
+  // Page id (table entry) for this lane's K token of tile k; slot returned.
+  __device__ __forceinline__ int fetch_page(int k, int& slot) const {
+    int t = min(tile_start(k) + r, s1 - 1);
+    int idx = div_page(t, p.page_size, p.inv_page_size, slot);
+    return tab[idx];
+  }
+
+  // Issue the K and V loads of a tile whose lane-token page/slot are known.
+  __device__ __forceinline__ void issue(TileRegs<FP8>& R, int page, int slot) {
+    bool ok = (page >= 0) & (page < p.num_pages);
+    bad |= !ok;
+    page = ok ? page : 0;
+    int64_t off = static_cast<int64_t>(page) * p.page_stride +
+                  static_cast<int64_t>(slot) * p.token_stride + head_off;
+    const uint8_t* krow = p.k_base + off;
+#pragma unroll
+    for (int i = 0; i < Geo<FP8>::kK; ++i) R.k[i] = load16(krow + 16 * (qd + 4 * i));
+    // V rows of tokens 4qd .. 4qd+3: their offsets come from the lanes that
+    // computed them for K.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      int64_t voff = __shfl(off, 4 * qd + e);
+      const uint8_t* vrow = p.v_base + voff + 16 * r;
+#pragma unroll
+      for (int c = 0; c < Geo<FP8>::kV; ++c) R.v[e][c] = load16(vrow + 256 * c);
+    }
+  }
+
+  __device__ __forceinline__ void process(const TileRegs<FP8>& R, int k) {
+    const int t0 = tile_start(k);
+    // ---- logits: S^T[token][head] on MFMA
+    f4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      h8_t kop;
+      if constexpr (FP8) {
+        kop = (st & 1) ? e4m3x8_to_h8<1>(R.k[st >> 1]) : e4m3x8_to_h8<0>(R.k[st >> 1]);
+      } else {
+        kop = __builtin_bit_cast(h8_t, R.k[st]);
+      }
+      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[st], s, 0, 0, 0);
+    }
+    // ---- online softmax, log2 domain
+    float z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int t = t0 + 4 * qd + i;
+      z[i] = (t < s1) ? s[i] * p.qk_scale_log2 : -__builtin_huge_valf();
+    }
+    float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);  // finite: the tile has a live token
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float pz[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pz[i] = __builtin_amdgcn_exp2f(z[i] - m_new);
+    l_run = l_run * alpha + ((pz[0] + pz[1]) + (pz[2] + pz[3]));
+    m_run = m_new;
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[j] *= alpha;
+    }
+    h4_t pop;
+    pop[0] = static_cast<_Float16>(pz[0]);
+    pop[1] = static_cast<_Float16>(pz[1]);
+    pop[2] = static_cast<_Float16>(pz[2]);
+    pop[3] = static_cast<_Float16>(pz[3]);
+    // ---- PV on MFMA
+    if constexpr (FP8) {
+      uint32_t hv[4][8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          hv[e][2 * w] = e4m3x2_to_f16x2<false>(R.v[e][0][w]);
+          hv[e][2 * w + 1] = e4m3x2_to_f16x2<true>(R.v[e][0][w]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int pw = j >> 1;
+        u2_t a;
+        if (j & 1) {
+          a[0] = hi_pair(hv[1][pw], hv[0][pw]);
+          a[1] = hi_pair(hv[3][pw], hv[2][pw]);
+        } else {
+          a[0] = lo_pair(hv[1][pw], hv[0][pw]);
+          a[1] = lo_pair(hv[3][pw], hv[2][pw]);
+        }
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4_t, a), pop,
+                                                       acc[j], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int c = j >> 3;
+        const int w = (j & 7) >> 1;
+        u2_t a;
+        if (j & 1) {
+          a[0] = hi_pair(R.v[1][c][w], R.v[0][c][w]);
+          a[1] = hi_pair(R.v[3][c][w], R.v[2][c][w]);
+        } else {
+          a[0] = lo_pair(R.v[1][c][w], R.v[0][c][w]);
+          a[1] = lo_pair(R.v[3][c][w], R.v[2][c][w]);
+        }
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4_t, a), pop,
+                                                       acc[j], 0, 0, 0);
+      }
+    }
+  }
+
+  // Head-dim index held by acc[j][i] of this lane.
+  __device__ __forceinline__ int out_dim(int j, int i) const {
+    const int m = 4 * qd + i;
+    if constexpr (FP8) return 16 * m + j;
+    return 128 * (j >> 3) + 8 * m + (j & 7);
+  }
+};
+
+template <bool FP8>
+__global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
+  extern __shared__ float smem[];
+  const int lane = threadIdx.x & 63;
+  // The wave index is uniform across the wave; saying so keeps the tile loop
+  // on scalar branches.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wg = blockIdx.x;
+  const int split = wg % p.splits;
+  const int bg = wg / p.splits;
+  const int b = bg / p.hkv;
+  const int g = bg - b * p.hkv;
+
+  const int L = min(p.lens[b], p.max_len);
+  const int s0 = split * p.chunk;
+  const int s1 = min(s0 + p.chunk, L);
+  if (p.splits > 1 && s0 >= L) return;  // split past the end: nothing to merge
+
+  Wave<FP8> W{p};
+  W.tab = p.table + static_cast<int64_t>(b) * p.max_pages;
+  W.head_off = static_cast<int64_t>(g) * p.head_stride;
+  W.s0 = s0;
+  W.s1 = s1;
+  W.wave = wave;
+  W.r = lane & 15;
+  W.qd = lane >> 4;
+  W.m_run = -__builtin_huge_valf();
+  W.l_run = 0.f;
+  W.bad = false;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) W.acc[j] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  // q^T operand: head r of the group (zero past the group), the head-dim
+  // pieces in the same permuted order as the K operand.
+  {
+    const int head = g * p.group + W.r;
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(
+        p.q + (static_cast<int64_t>(b) * p.hq + (W.r < p.group ? head : 0)) * kHeadDim);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int d0 = FP8 ? 16 * (W.qd + 4 * (st >> 1)) + 8 * (st & 1) : 8 * (W.qd + 4 * st);
+      u4_t v = load16(qrow + 2 * d0);
+      if (W.r >= p.group) v = u4_t{0u, 0u, 0u, 0u};
+      W.qop[st] = __builtin_bit_cast(h8_t, v);
+    }
+  }
+
+  const int span = s1 - s0 - wave * kTile;
+  const int ntiles = span > 0 ? (span + kWaves * kTile - 1) / (kWaves * kTile) : 0;
+
+  // Software pipeline: while tile k is computed, tile k+1's K/V loads and
+  // tile k+2's page-table entries are in flight.  The page-table load of tile
+  // k+2 is issued before the K/V loads of tile k+1, so waiting for it later
+  // (loads complete in issue order) never drains tile k+1's loads.  The
+  // steady-state loop is straight-line so the wait counters stay precise; the
+  // last one to three tiles are peeled off after it.
+  if (ntiles > 0) {
+    TileRegs<FP8> A, B;
+    int slotA, slotB;
+    int pageA = W.fetch_page(0, slotA);
+    int pageB = W.fetch_page(1, slotB);
+    W.issue(A, pageA, slotA);
+    int k = 0;
+    for (; k + 3 < ntiles; k += 2) {
+      pageA = W.fetch_page(k + 2, slotA);
+      W.issue(B, pageB, slotB);
+      W.process(A, k);
+      pageB = W.fetch_page(k + 3, slotB);
+      W.issue(A, pageA, slotA);
+      W.process(B, k + 1);
+    }
+    // ntiles - k is 1, 2 or 3; A holds tile k, pageB is tile k+1's.
+    const bool has1 = k + 1 < ntiles;
+    const bool has2 = k + 2 < ntiles;
+    if (has1) {
+      pageA = W.fetch_page(k + 2, slotA);
+      W.issue(B, pageB, slotB);
+    }
+    W.process(A, k);
+    if (has1) {
+      if (has2) W.issue(A, pageA, slotA);
+      W.process(B, k + 1);
+      if (has2) W.process(A, k + 2);
+    }
+  }
+
+  // ---- merge the four waves through LDS
+  const int group = p.group;
+  float* so = smem;                               // [kWaves][group][kLdsRow]
+  float* sm = so + kWaves * group * kLdsRow;      // [kWaves][16]
+  float* sl = sm + kWaves * 16;                   // [kWaves][16]
+  int* sbad = reinterpret_cast<int*>(sl + kWaves * 16);  // [kWaves]
+  float l_tot = W.l_run + __shfl_xor(W.l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  const bool wave_bad = __ballot(W.bad) != 0;
+  if (W.r < group) {
+    float* row = so + (wave * group + W.r) * kLdsRow;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) row[W.out_dim(j, i)] = W.acc[j][i];
+    }
+    if (W.qd == 0) {
+      sm[wave * 16 + W.r] = W.m_run;
+      sl[wave * 16 + W.r] = l_tot;
+    }
+  }
+  if (lane == 0) sbad[wave] = wave_bad ? 1 : 0;
+  __syncthreads();
+
+  const int d = threadIdx.x;  // kThreads == kHeadDim
+  const bool any_bad = (sbad[0] | sbad[1] | sbad[2] | sbad[3]) != 0;
+  for (int h = 0; h < group; ++h) {
+    float M = -__builtin_huge_valf();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * 16 + h]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm[w * 16 + h];
+      if (mw != -__builtin_huge_valf()) {
+        const float e = __builtin_amdgcn_exp2f(mw - M);
+        num += e * so[(w * group + h) * kLdsRow + d];
+        den += e * sl[w * 16 + h];
+      }
+    }
+    const int64_t oh = static_cast<int64_t>(b) * p.hq + g * group + h;
+    if (p.splits == 1) {
+      float o = den > 0.f ? (num / den) * p.v_scale : 0.f;
+      if (any_bad) o = __builtin_nanf("");
+      p.out[oh * kHeadDim + d] = f16_bits(o);
+    } else {
+      float o = num / den;
+      if (any_bad) o = __builtin_nanf("");
+      p.ws_o[(oh * p.splits + split) * kHeadDim + d] = o;
+      if (d == 0) p.ws_lse[oh * p.splits + split] = M + __log2f(den);
+    }
+  }
+}
+
+// Merge the split partials of one (sequence, query head): weights 2^(lse_s - max).
+__global__ __launch_bounds__(kHeadDim) void combine_kernel(AttnParams p) {
+  const int oh = blockIdx.x;
+  const int b = oh / p.hq;
+  const int d = threadIdx.x;
+  const int L = min(p.lens[b], p.max_len);
+  const int nact = L > 0 ? (L + p.chunk - 1) / p.chunk : 0;
+  float o = 0.f;
+  if (nact > 0) {
+    const float* lse = p.ws_lse + static_cast<int64_t>(oh) * p.splits;
+    float M = -__builtin_huge_valf();
+    for (int s = 0; s < nact; ++s) M = fmaxf(M, lse[s]);
+    float num = 0.f, den = 0.f;
+    const float* po = p.ws_o + static_cast<int64_t>(oh) * p.splits * kHeadDim + d;
+    for (int s = 0; s < nact; ++s) {
+      const float e = __builtin_amdgcn_exp2f(lse[s] - M);
+      num += e * po[static_cast<int64_t>(s) * kHeadDim];
+      den += e;
+    }
+    o = (num / den) * p.v_scale;
+  }
+  p.out[static_cast<int64_t>(oh) * kHeadDim + d] = f16_bits(o);
+}
+
+__global__ void e4m3_table_kernel(float* out) {
+  const int c = threadIdx.x;
+  const uint32_t h = e4m3x2_to_f16x2<false>(static_cast<uint32_t>(c));
+  out[c] = static_cast<float>(__builtin_bit_cast(h2_t, h)[0]);
+}
+
+}  // namespace
+
+size_t attention_lds_bytes(int group) {
+  return sizeof(float) * (static_cast<size_t>(kWaves) * group * kLdsRow + 2 * kWaves * 16) +
+         sizeof(int) * kWaves;
+}
+
+// Kernels whose merge buffer exceeds the default 64 KiB dynamic LDS limit
+// (groups of more than 12 heads) need the limit raised once per process.
+static hipError_t allow_large_lds() {
+  static hipError_t status = [] {
+    const int bytes = static_cast<int>(attention_lds_bytes(kMaxGroup));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attention_kernel<true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(attention_kernel<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    return e;
+  }();
+  return status;
+}
+
+hipError_t launch_attention(const AttnParams& p, bool fp8, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(p.splits) * p.n * p.hkv);
+  const size_t lds = attention_lds_bytes(p.group);
+  if (lds > 65536) {
+    hipError_t e = allow_large_lds();
+    if (e != hipSuccess) return e;
+  }
+  if (fp8) {
+    hipLaunchKernelGGL(attention_kernel<true>, grid, dim3(kThreads), lds, stream, p);
+  } else {
+    hipLaunchKernelGGL(attention_kernel<false>, grid, dim3(kThreads), lds, stream, p);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.splits == 1) return err;
+  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(p.n) * p.hq), dim3(kHeadDim), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_e4m3_table(float* out256, hipStream_t stream) {
+  hipLaunchKernelGGL(e4m3_table_kernel, dim3(1), dim3(256), 0, stream, out256);
+  return hipGetLastError();
+}
+
+}  // namespace pgqa

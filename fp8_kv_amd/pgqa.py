@@ -1,0 +1,216 @@
+"""ctypes binding of libpgqa (include/pgqa.h): argument marshalling only.
+
+Every function has the name of the C entry point it calls.  Tensors are
+torch tensors on the GPU (PyTorch provides device memory and streams); the
+computation is done entirely by the library's HIP kernels.  There is no
+fallback: if ``libpgqa.so`` is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpgqa.so")
+
+PGQA_OK = 0
+PGQA_ERR_NULL = -1
+PGQA_ERR_SHAPE = -2
+PGQA_ERR_LAYOUT = -3
+PGQA_ERR_DTYPE = -4
+PGQA_ERR_WORKSPACE = -5
+PGQA_ERR_HIP = -6
+PGQA_ERR_ARG = -7
+PGQA_KV_FP16 = 0
+PGQA_KV_E4M3 = 1
+HEAD_DIM = 256
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+# Every symbol include/pgqa.h declares.
+EXPORTS = ("paged_gqa_workspace_bytes", "paged_gqa_num_splits", "paged_gqa_decode",
+           "paged_gqa_prefill_sparse", "e4m3_decode_table", "pgqa_error_string")
+
+
+class PgqaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = _lib().pgqa_error_string(code).decode() if _LIB else str(code)
+        super().__init__(f"{where}: {msg} (code {code})")
+        self.code = code
+
+
+class KVPoolC(ctypes.Structure):
+    """Mirror of pgqa_kv_pool."""
+    _fields_ = [
+        ("k_base", ctypes.c_void_p), ("v_base", ctypes.c_void_p),
+        ("page_stride", ctypes.c_int64), ("token_stride", ctypes.c_int64),
+        ("head_stride", ctypes.c_int64), ("num_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+    ]
+
+
+_LIB = None
+
+
+def _lib(path: str = LIB_PATH) -> ctypes.CDLL:
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is not built; run `python -m fp8_kv_amd.build` (there is no fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    lib.paged_gqa_workspace_bytes.restype = sz
+    lib.paged_gqa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.paged_gqa_num_splits.restype = i32
+    lib.paged_gqa_num_splits.argtypes = [i32, i32, i32, i32]
+    attn_args = [vp, ctypes.POINTER(KVPoolC), vp, i32, vp, i32, i32, i32, i32, i32, f32, i32,
+                 vp, vp, sz, vp]
+    for name in ("paged_gqa_decode", "paged_gqa_prefill_sparse"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = attn_args
+    lib.e4m3_decode_table.restype = ctypes.c_int
+    lib.e4m3_decode_table.argtypes = [vp, vp]
+    lib.pgqa_error_string.restype = ctypes.c_char_p
+    lib.pgqa_error_string.argtypes = [ctypes.c_int]
+    _LIB = lib
+    return lib
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    return _lib(path)
+
+
+@dataclass
+class KVPool:
+    """A paged KV pool in device memory.  `k` and `v` are tensors whose
+    data_ptr() is the address of K/V element (page 0, slot 0, head 0, dim 0);
+    strides are in elements (see pgqa_kv_pool in include/pgqa.h)."""
+
+    k: object
+    v: object
+    page_stride: int
+    token_stride: int
+    head_stride: int
+    num_pages: int
+    page_size: int
+    kv_dtype: int
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    storage: tuple = ()  # tensors kept alive with the pool
+
+    def as_c(self) -> KVPoolC:
+        return KVPoolC(self.k.data_ptr(), self.v.data_ptr(), self.page_stride,
+                       self.token_stride, self.head_stride, self.num_pages, self.page_size,
+                       self.kv_dtype, self.k_scale, self.v_scale)
+
+
+def _stream_handle(stream) -> int | None:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != PGQA_OK:
+        raise PgqaError(rc, where)
+
+
+def paged_gqa_workspace_bytes(n: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int,
+                              num_splits: int = 0, head_dim: int = HEAD_DIM) -> int:
+    r = _lib().paged_gqa_workspace_bytes(n, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                         num_splits)
+    if r == SIZE_MAX:
+        raise PgqaError(PGQA_ERR_ARG, "paged_gqa_workspace_bytes")
+    return int(r)
+
+
+def paged_gqa_num_splits(n: int, num_kv_heads: int, max_seq_len: int, num_splits: int = 0) -> int:
+    r = _lib().paged_gqa_num_splits(n, num_kv_heads, max_seq_len, num_splits)
+    if r < 0:
+        raise PgqaError(r, "paged_gqa_num_splits")
+    return int(r)
+
+
+def paged_gqa_decode(q, kv: KVPool, page_table, seq_lens, max_seq_len: int, sm_scale: float,
+                     out, num_kv_heads: int = 1, workspace=None, num_splits: int = 0,
+                     stream=None) -> None:
+    """q, out: fp16 [B][Hq][256]; page_table: int32 [B][max_pages];
+    seq_lens: int32 [B]; workspace: any device tensor of at least
+    paged_gqa_workspace_bytes(...) bytes (None when that is 0)."""
+    _call("paged_gqa_decode", q, kv, page_table, seq_lens, max_seq_len, num_kv_heads, sm_scale,
+          num_splits, out, workspace, stream)
+
+
+def paged_gqa_prefill_sparse(q, kv: KVPool, row_tables, row_lens, max_row_len: int,
+                             sm_scale: float, out, num_kv_heads: int = 1, workspace=None,
+                             num_splits: int = 0, stream=None) -> None:
+    """Sparse prefill: rows in place of sequences (see include/pgqa.h)."""
+    _call("paged_gqa_prefill_sparse", q, kv, row_tables, row_lens, max_row_len, num_kv_heads,
+          sm_scale, num_splits, out, workspace, stream)
+
+
+def _call(fn_name, q, kv, table, lens, max_len, hkv, sm_scale, num_splits, out, workspace,
+          stream):
+    n, hq, d = q.shape
+    c_pool = kv.as_c()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = getattr(_lib(), fn_name)(
+        _ptr(q), ctypes.byref(c_pool), _ptr(table), int(table.shape[1]), _ptr(lens),
+        int(max_len), int(n), int(hq), int(hkv), int(d), float(sm_scale), int(num_splits),
+        _ptr(out), _ptr(workspace), int(ws_bytes), _stream_handle(stream))
+    _check(rc, fn_name)
+
+
+def e4m3_decode_table(out, stream=None) -> None:
+    """out: float32 [256] device tensor."""
+    _check(_lib().e4m3_decode_table(_ptr(out), _stream_handle(stream)), "e4m3_decode_table")
+
+
+# ------------------------------------------------------------ device inputs
+def device_case(case, device="cuda"):
+    """Copy a host PagedCase (fp8_kv_amd.inputs) to device memory.
+
+    Returns (q, pool, table, lens) as device tensors / KVPool."""
+    import torch
+
+    q = torch.from_numpy(case.q).to(device)
+    ks = torch.from_numpy(case.k_store).to(device)
+    if case.v_store is case.k_store:
+        vs = ks
+    else:
+        vs = torch.from_numpy(case.v_store).to(device)
+    kflat, vflat = ks.reshape(-1), vs.reshape(-1)
+    pool = KVPool(k=kflat[case.k_offset:], v=vflat[case.v_offset:],
+                  page_stride=case.page_stride, token_stride=case.token_stride,
+                  head_stride=case.head_stride, num_pages=case.num_pages,
+                  page_size=case.page_size, kv_dtype=case.kv_dtype, k_scale=case.k_scale,
+                  v_scale=case.v_scale, storage=(ks, vs))
+    table = torch.from_numpy(case.table).to(device)
+    lens = torch.from_numpy(case.lens).to(device)
+    return q, pool, table, lens
+
+
+def run_case(case, *, prefill: bool = False, num_splits: int = 0, device="cuda", stream=None):
+    """Run one PagedCase through the library; returns the fp16 output tensor."""
+    import torch
+
+    q, pool, table, lens = device_case(case, device)
+    n, hq, _ = q.shape
+    out = torch.empty_like(q)
+    wsb = paged_gqa_workspace_bytes(n, hq, case.num_kv_heads, case.max_seq_len, num_splits)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=device) if wsb else None
+    fn = paged_gqa_prefill_sparse if prefill else paged_gqa_decode
+    fn(q, pool, table, lens, case.max_seq_len, case.sm_scale, out,
+       num_kv_heads=case.num_kv_heads, workspace=ws, num_splits=num_splits, stream=stream)
+    return out

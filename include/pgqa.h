@@ -1,0 +1,172 @@
+/*
+ * pgqa.h -- C ABI of libpgqa, paged grouped-query attention for MI355X (gfx950).
+ *
+ * The operation (by page title and section):
+ *   - "[Kernel][SM70] Scale NVFP4 E4M3 decode batches", Purpose: decode
+ *     attention for batches of sequences where a group of 6 query heads shares
+ *     one KV head of dimension 256, K/V gathered through a page table from a
+ *     paged pool stored as FP8-E4M3, including long contexts.
+ *   - "[Kernel][SM70] Accelerate Qwen3.8 QSA paged prefill", Changes: sparse
+ *     prefill, where each query row attends to its selected tokens exposed as
+ *     a virtual page table of 4-token pages into a shared FP16 pool; K/V may
+ *     use contiguous or interleaved strides; rows are clamped to their live
+ *     length and empty rows are inert.
+ * For every sequence (or row) b, query head h and kv head g = h / (Hq/Hkv):
+ *     z_t = sm_scale * <q[b][h], K_t>,   t = 0 .. L_b - 1
+ *     out[b][h] = sum_t exp(z_t - max z) V_t / sum_t exp(z_t - max z)
+ * where logical token t lives in physical page page_table[b][t / page_size],
+ * slot t % page_size, and K_t, V_t are the pool rows there for kv head g.  For
+ * FP8 pools the real value of a stored code c is k_scale * E4M3(c) (K) and
+ * v_scale * E4M3(c) (V), E4M3 being the OCP E4M3FN format.  L_b <= 0 gives a
+ * zero output row and reads no KV.
+ *
+ * Conventions shared by every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or retains them.  `stream` is a hipStream_t (NULL
+ *     = the default stream).  Work is enqueued asynchronously: a return of
+ *     PGQA_OK means the launch was accepted, and device faults surface at the
+ *     caller's next synchronisation, as usual in HIP.
+ *   - On any error code nothing is launched and no output is written.
+ *   - Thread-safe and stateless apart from a per-device cache of the compute
+ *     unit count.  Calls may be captured into HIP graphs (no allocation, no
+ *     synchronisation, no memset inside).
+ */
+#ifndef PGQA_H
+#define PGQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define PGQA_OK 0
+#define PGQA_ERR_NULL (-1)      /* a required pointer is NULL                        */
+#define PGQA_ERR_SHAPE (-2)     /* head_dim != 256, Hq not 1..16 x Hkv, bad sizes     */
+#define PGQA_ERR_LAYOUT (-3)    /* pointer or stride not 16-byte aligned, bad strides */
+#define PGQA_ERR_DTYPE (-4)     /* kv_dtype is neither PGQA_KV_FP16 nor PGQA_KV_E4M3  */
+#define PGQA_ERR_WORKSPACE (-5) /* workspace missing or smaller than required         */
+#define PGQA_ERR_HIP (-6)       /* the HIP runtime refused a query or a launch        */
+#define PGQA_ERR_ARG (-7)       /* non-finite scale, negative split count, ...        */
+
+/* KV element formats. */
+#define PGQA_KV_FP16 0 /* IEEE binary16; k_scale / v_scale are ignored           */
+#define PGQA_KV_E4M3 1 /* OCP FP8 E4M3FN codes (uint8); real = scale * E4M3(c)  */
+
+#define PGQA_HEAD_DIM 256
+#define PGQA_MAX_GROUP 16         /* query heads per kv head                 */
+#define PGQA_MAX_SEQ_LEN 4194304  /* tokens per sequence or row (2^22)       */
+
+/*
+ * A paged KV pool.  Element (page p, slot t, kv head g, dim d) of K is at
+ *     (elem*)k_base + p*page_stride + t*token_stride + g*head_stride + d
+ * and likewise for V from v_base; strides are in elements and d is unit
+ * stride.  This covers, for a pool [num_pages][P][Hkv][256]:
+ *   contiguous  (separate K and V arrays): page_stride = P*Hkv*256,
+ *               token_stride = Hkv*256, head_stride = 256;
+ *   interleaved (one array [num_pages][2][P][Hkv][256], K block then V block
+ *               in every page): v_base = k_base + P*Hkv*256 elements,
+ *               page_stride = 2*P*Hkv*256;
+ *   head-major  ([num_pages][Hkv][P][256]): token_stride = 256,
+ *               head_stride = P*256.
+ * k_base, v_base and every stride in bytes must be multiples of 16.
+ */
+typedef struct pgqa_kv_pool {
+  const void* k_base;
+  const void* v_base;
+  int64_t page_stride;
+  int64_t token_stride;
+  int64_t head_stride;
+  int32_t num_pages;  /* valid page ids are 0 .. num_pages-1 (>= 1)       */
+  int32_t page_size;  /* tokens per page, >= 1                            */
+  int32_t kv_dtype;   /* PGQA_KV_FP16 or PGQA_KV_E4M3                     */
+  float k_scale;      /* per-tensor multipliers, FP8 only, must be finite */
+  float v_scale;
+} pgqa_kv_pool;
+
+/*
+ * Bytes of workspace a decode or prefill call needs for `n` sequences/rows,
+ * `num_q_heads` heads and `max_seq_len`, with `num_splits` (0 = the automatic
+ * choice for the current device).  Returns 0 when no workspace is needed
+ * (a single split) and SIZE_MAX on invalid arguments or a HIP query failure.
+ * The workspace holds split partials only; it needs no initialisation.
+ */
+size_t paged_gqa_workspace_bytes(int32_t n, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len, int32_t num_splits);
+
+/*
+ * Split count a call with these arguments would use (num_splits = 0 means the
+ * automatic choice for the current device).  Returns < 0 on invalid arguments.
+ */
+int32_t paged_gqa_num_splits(int32_t n, int32_t num_kv_heads, int32_t max_seq_len,
+                             int32_t num_splits);
+
+/*
+ * Paged GQA decode (source: "[Kernel][SM70] Scale NVFP4 E4M3 decode batches",
+ * Purpose -- batched paged decode with FP8-E4M3 KV and long-context routes).
+ *
+ * q          : fp16 [batch][num_q_heads][256], contiguous, 16-byte aligned.
+ * kv         : host pointer to the pool description (read during the call only).
+ * page_table : int32 [batch][max_pages], row-major; only the first
+ *              ceil(min(L_b, max_seq_len) / page_size) entries of row b are read.
+ *              An entry outside [0, num_pages) is never dereferenced: the
+ *              affected output row becomes NaN instead.
+ * seq_lens   : int32 [batch]; L_b <= 0 gives zeros; L_b is clamped to max_seq_len.
+ * max_seq_len: host-side bound on the lengths (sizes the grid and the split
+ *              plan); must satisfy max_seq_len <= max_pages * page_size and
+ *              max_seq_len <= PGQA_MAX_SEQ_LEN.
+ * num_q_heads: group * num_kv_heads with 1 <= group <= 16 (6 in the pages).
+ * head_dim   : must be 256.
+ * sm_scale   : softmax scale applied to q.K (finite).
+ * num_splits : number of key-range splits per (sequence, kv head), 0 = auto.
+ *              More than one split writes per-split partials to `workspace`
+ *              and a second kernel merges them with their log-sum-exp.
+ * out        : fp16 [batch][num_q_heads][256], contiguous, 16-byte aligned;
+ *              must not alias q.
+ * workspace  : device scratch of at least paged_gqa_workspace_bytes(...) bytes
+ *              (may be NULL when that is 0), 16-byte aligned, not shared with
+ *              a concurrently running call.
+ */
+int paged_gqa_decode(const void* q, const pgqa_kv_pool* kv, const int32_t* page_table,
+                     int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len,
+                     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, float sm_scale, int32_t num_splits, void* out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse paged prefill (source: "[Kernel][SM70] Accelerate Qwen3.8 QSA paged
+ * prefill", Changes -- every query row attends to the tokens its virtual
+ * page-4 table selects, with no KV copy).
+ *
+ * Same contract as paged_gqa_decode with query rows in place of sequences:
+ * q and out are [rows][num_q_heads][256]; row_tables is int32
+ * [rows][max_pages], each row listing the physical pages (normally page_size 4:
+ * the selected 4-token blocks in increasing order, then the causal partial
+ * page) whose first row_lens[r] tokens the row attends to; max_row_len bounds
+ * row_lens.  The result for a row equals paged_gqa_decode on the same table
+ * and length.
+ */
+int paged_gqa_prefill_sparse(const void* q, const pgqa_kv_pool* kv, const int32_t* row_tables,
+                             int32_t max_pages, const int32_t* row_lens, int32_t max_row_len,
+                             int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, float sm_scale, int32_t num_splits, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Writes to out256[c] (device, fp32 [256]) the value the attention kernels'
+ * E4M3 dequantisation gives code c with a unit scale (source: "[Kernel][SM70]
+ * Scale NVFP4 E4M3 decode batches", Audit fixes -- the E4M3 converter is
+ * part of the decode path).  The two NaN codes yield NaN.
+ */
+int e4m3_decode_table(float* out256, void* stream);
+
+/* Static description of a return code. */
+const char* pgqa_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PGQA_H */

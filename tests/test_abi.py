@@ -1,0 +1,141 @@
+"""The C ABI on the CPU: the library loads, exports every symbol pgqa.h
+declares, and rejects bad arguments before any HIP call (no GPU needed)."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from fp8_kv_amd import pgqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pgqa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pgqa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"defined"})
+
+
+def test_header_and_binding_agree():
+    assert sorted(pgqa.EXPORTS) == declared_functions()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name in ("PGQA_OK", "PGQA_ERR_NULL", "PGQA_ERR_SHAPE", "PGQA_ERR_LAYOUT",
+                 "PGQA_ERR_DTYPE", "PGQA_ERR_WORKSPACE", "PGQA_ERR_HIP", "PGQA_ERR_ARG",
+                 "PGQA_KV_FP16", "PGQA_KV_E4M3"):
+        m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
+        assert m and int(m.group(1)) == getattr(pgqa, name), name
+
+
+def test_struct_layout():
+    # pgqa_kv_pool: 2 pointers, 3 int64, 3 int32, 2 float, padded to 8 bytes.
+    C = pgqa.KVPoolC
+    assert [C.page_stride.offset, C.num_pages.offset, C.kv_dtype.offset, C.v_scale.offset] == \
+        [16, 40, 48, 56]
+    assert ctypes.sizeof(C) == 64
+
+
+# Fake, aligned, never-dereferenced device addresses: validation must reject
+# the call before touching them.
+FAKE = 1 << 20
+
+
+def pool(**kw):
+    base = dict(k_base=FAKE, v_base=FAKE + 4096, page_stride=16 * 256, token_stride=256,
+                head_stride=256, num_pages=8, page_size=16, kv_dtype=pgqa.PGQA_KV_E4M3,
+                k_scale=1.0, v_scale=1.0)
+    base.update(kw)
+    return pgqa.KVPoolC(**base)
+
+
+def call(lib, fn="paged_gqa_decode", q=FAKE, kv=None, table=FAKE, max_pages=64, lens=FAKE,
+         max_len=1024, n=2, hq=6, hkv=1, d=256, sm=0.0625, splits=0, out=FAKE * 2, ws=None,
+         ws_bytes=0):
+    kv = pool() if kv is None else kv
+    return getattr(lib, fn)(q, ctypes.byref(kv), table, max_pages, lens, max_len, n, hq, hkv, d,
+                            sm, splits, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["paged_gqa_decode", "paged_gqa_prefill_sparse"])
+def test_validation_errors(lib, fn):
+    E = pgqa
+    c = lambda **kw: call(lib, fn, **kw)  # noqa: E731
+    assert c(q=None) == E.PGQA_ERR_NULL
+    assert c(out=None) == E.PGQA_ERR_NULL
+    assert c(table=None) == E.PGQA_ERR_NULL
+    assert c(lens=None) == E.PGQA_ERR_NULL
+    assert c(kv=pool(k_base=None)) == E.PGQA_ERR_NULL
+    assert getattr(lib, fn)(FAKE, None, FAKE, 64, FAKE, 1024, 2, 6, 1, 256, 0.0625, 0, FAKE,
+                            None, 0, None) == E.PGQA_ERR_NULL
+    assert c(d=128) == E.PGQA_ERR_SHAPE
+    assert c(hq=17, hkv=1) == E.PGQA_ERR_SHAPE
+    assert c(hq=6, hkv=4) == E.PGQA_ERR_SHAPE
+    assert c(hkv=0) == E.PGQA_ERR_SHAPE
+    assert c(n=-1) == E.PGQA_ERR_SHAPE
+    assert c(max_len=1025) == E.PGQA_ERR_SHAPE        # > max_pages * page_size
+    assert c(max_len=1 << 23, max_pages=1 << 20) == E.PGQA_ERR_SHAPE  # > PGQA_MAX_SEQ_LEN
+    assert c(max_len=-1) == E.PGQA_ERR_SHAPE
+    assert c(kv=pool(page_size=0)) == E.PGQA_ERR_SHAPE
+    assert c(kv=pool(num_pages=0)) == E.PGQA_ERR_SHAPE
+    assert c(kv=pool(kv_dtype=2)) == E.PGQA_ERR_DTYPE
+    assert c(kv=pool(k_base=FAKE + 8)) == E.PGQA_ERR_LAYOUT
+    assert c(kv=pool(token_stride=264)) == E.PGQA_ERR_LAYOUT   # 264 B, not 16-aligned
+    assert c(kv=pool(page_stride=-4096)) == E.PGQA_ERR_LAYOUT
+    assert c(q=FAKE + 2) == E.PGQA_ERR_LAYOUT
+    assert c(splits=-1) == E.PGQA_ERR_ARG
+    assert c(sm=math.nan) == E.PGQA_ERR_ARG
+    assert c(kv=pool(k_scale=math.inf)) == E.PGQA_ERR_ARG
+    # FP16 ignores the scales, so a non-finite one is accepted there: the
+    # call then fails only for want of a workspace.
+    assert c(kv=pool(kv_dtype=pgqa.PGQA_KV_FP16, k_scale=math.inf, token_stride=256),
+             splits=4) == E.PGQA_ERR_WORKSPACE
+    # Explicit splits need no device query; the workspace is checked.
+    assert c(splits=4) == E.PGQA_ERR_WORKSPACE
+    need = lib.paged_gqa_workspace_bytes(2, 6, 1, 256, 1024, 4)
+    assert need == 2 * 6 * 4 * 257 * 4
+    assert c(splits=4, ws=FAKE * 4, ws_bytes=need - 1) == E.PGQA_ERR_WORKSPACE
+    assert c(splits=4, ws=FAKE * 4 + 8, ws_bytes=need) == E.PGQA_ERR_WORKSPACE
+    # Nothing to do: accepted without any HIP call.
+    assert c(n=0, q=None, out=None, table=None, lens=None) == E.PGQA_OK
+
+
+def test_workspace_bytes(lib):
+    ws = lib.paged_gqa_workspace_bytes
+    assert ws(16, 6, 1, 256, 16384, 32) == 16 * 6 * 32 * 257 * 4
+    assert ws(16, 6, 1, 256, 16384, 1) == 0
+    assert ws(16, 6, 1, 128, 16384, 4) == pgqa.SIZE_MAX
+    assert ws(16, 6, 1, 256, -5, 4) == pgqa.SIZE_MAX
+    # More splits than 64-token chunks are capped.
+    assert lib.paged_gqa_num_splits(1, 1, 100, 50) == 2
+    assert lib.paged_gqa_num_splits(1, 1, 16384, 32) == 32
+    assert lib.paged_gqa_num_splits(1, 1, 16384, 7) == 7
+    assert lib.paged_gqa_num_splits(1, 1, 0, 3) == 1
+    assert lib.paged_gqa_num_splits(1, 0, 10, 3) < 0
+
+
+def test_e4m3_table_rejects_null(lib):
+    assert lib.e4m3_decode_table(None, None) == pgqa.PGQA_ERR_NULL
+    assert lib.e4m3_decode_table(FAKE + 4, None) == pgqa.PGQA_ERR_LAYOUT
+
+
+def test_error_strings(lib):
+    for code in range(-7, 1):
+        assert lib.pgqa_error_string(code)
+    assert lib.pgqa_error_string(-99) == b"unknown error code"

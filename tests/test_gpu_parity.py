@@ -1,0 +1,258 @@
+"""GPU parity: libpgqa's HIP kernels against the fp64 oracle, through the C ABI.
+
+Every case is seeded synthetic data from fp8_kv_amd.inputs; the oracle sees
+the same host arrays the GPU receives.  Bar: max abs <= 2e-3 and rel L2 <=
+1e-3 on the fp16 output (tests/parity.py).  Integer-exact properties (layout,
+page permutation, determinism, graph replay, prefill = decode) are checked
+bitwise.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from fp8_kv_amd import inputs
+from tests.parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+E4M3, FP16 = inputs.KV_E4M3, inputs.KV_FP16
+
+
+@pytest.fixture(scope="module")
+def pg():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from fp8_kv_amd import pgqa
+
+    pgqa.load()  # raises if libpgqa.so is missing: there is no fallback
+    return pgqa
+
+
+def _run(pg, case, **kw):
+    import torch
+
+    out = pg.run_case(case, **kw)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _check(pg, case, what, seq_ids=None, **kw):
+    got = _run(pg, case, **kw)
+    ref = oracle.paged_gqa(**case.oracle_kwargs(), seq_ids=seq_ids)
+    if seq_ids is not None:
+        got = got[seq_ids]
+    assert_parity(got, ref, what)
+    return got
+
+
+# ---------------------------------------------------------------- E4M3 table
+def test_e4m3_table_matches_oracle(pg):
+    import torch
+
+    out = torch.empty(256, dtype=torch.float32, device="cuda")
+    pg.e4m3_decode_table(out)
+    got = out.cpu().numpy().astype(np.float64)
+    ref = oracle.e4m3_table()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+
+
+# ------------------------------------------------------------ the workloads
+@pytest.mark.parametrize("name", ["decode_b1_1k_fp16_p16", "decode_b8_1k_e4m3_p64",
+                                  "decode_b16_16k_e4m3_p128"])
+def test_workload_decode(pg, name):
+    case = inputs.workload_case(name)
+    _check(pg, case, name)
+
+
+@pytest.mark.parametrize("kv_dtype", [E4M3, FP16])
+@pytest.mark.parametrize("layout", ["contiguous", "interleaved"])
+def test_workload_ragged(pg, kv_dtype, layout):
+    case = inputs.workload_case("decode_ragged_b16_16k_p256", kv_dtype=kv_dtype, layout=layout)
+    assert not np.all(np.diff(case.table[0]) == 1)  # nonmonotonic tables
+    _check(pg, case, f"ragged {kv_dtype} {layout}")
+
+
+def test_workload_sparse_prefill_sampled(pg):
+    case = inputs.workload_case("prefill_sparse_4096x2051_p4")
+    rng = np.random.default_rng(1)
+    ids = np.unique(np.concatenate([[0, 1, case.n - 1],
+                                    rng.choice(case.n, 509, replace=False)])).astype(np.int32)
+    got = _run(pg, case, prefill=True)
+    ref = oracle.paged_gqa(**case.oracle_kwargs(), seq_ids=ids)
+    assert_parity(got[ids], ref, "prefill 4096x2051 sampled rows")
+    assert np.isfinite(got).all()
+
+
+# --------------------------------------------------------- shape coverage
+@pytest.mark.parametrize("kv_dtype", [E4M3, FP16])
+@pytest.mark.parametrize("page_size", [4, 5, 16, 64, 128, 256])
+def test_page_sizes_ragged_tails(pg, kv_dtype, page_size):
+    # Lengths cover one partial tile, several tiles and a ragged tail.
+    lens = [1, 15, 16, 17, 63, 64, 65, 200, 1000, 777]
+    case = inputs.decode_case(batch=len(lens), lens=lens, page_size=page_size,
+                              kv_dtype=kv_dtype, seed=page_size, scales="uniform")
+    for s in (1, 3, 0):
+        _check(pg, case, f"P{page_size} dtype{kv_dtype} splits{s}", num_splits=s)
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "interleaved", "head_major"])
+@pytest.mark.parametrize("kv_dtype", [E4M3, FP16])
+def test_multi_kv_head_layouts(pg, layout, kv_dtype):
+    case = inputs.decode_case(batch=3, lens=[300, 129, 1], page_size=32, kv_dtype=kv_dtype,
+                              layout=layout, num_q_heads=12, num_kv_heads=2, seed=21,
+                              scales="uniform")
+    _check(pg, case, f"hkv2 {layout} {kv_dtype}")
+
+
+@pytest.mark.parametrize("group", [1, 2, 8, 16])
+def test_group_sizes(pg, group):
+    case = inputs.decode_case(batch=2, lens=[333, 70], page_size=16, kv_dtype=E4M3,
+                              num_q_heads=group * 2, num_kv_heads=2, seed=30 + group,
+                              scales="uniform")
+    _check(pg, case, f"group {group}", num_splits=2)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 0])
+def test_split_counts_long_context(pg, splits):
+    case = inputs.decode_case(batch=2, lens=[5000, 4097], page_size=128, kv_dtype=E4M3,
+                              seed=40, scales="uniform")
+    _check(pg, case, f"splits {splits}", num_splits=splits)
+
+
+def test_sparse_prefill_tails(pg):
+    for tail in (1, 2, 3, 0):
+        case = inputs.sparse_prefill_case(rows=64, selected_blocks=40, tail=tail,
+                                          pool_blocks=512, seed=50 + tail)
+        _check(pg, case, f"prefill tail {tail}", prefill=True)
+
+
+def test_sparse_prefill_fp8_contiguous(pg):
+    case = inputs.sparse_prefill_case(rows=48, selected_blocks=100, tail=3, pool_blocks=400,
+                                      layout="contiguous", kv_dtype=E4M3, scales="uniform",
+                                      seed=55)
+    _check(pg, case, "prefill fp8 contiguous", prefill=True)
+
+
+# ----------------------------------------------------------- special cases
+def test_length_one_is_v(pg):
+    case = inputs.decode_case(batch=4, lens=1, page_size=16, kv_dtype=E4M3, seed=60,
+                              scales=(1.25, 0.5))
+    got = _run(pg, case)
+    ref = oracle.paged_gqa(**case.oracle_kwargs())
+    # o = V_0 * v_scale exactly, rounded once to fp16.
+    assert np.array_equal(got, ref.astype(np.float16))
+
+
+def test_empty_and_negative_lengths_are_zero(pg):
+    case = inputs.decode_case(batch=4, lens=[0, 50, -7, 0], page_size=16, kv_dtype=FP16,
+                              seed=61, max_seq_len=64)
+    t = case.table.copy()
+    t[[0, 2, 3]] = -1  # never read
+    case = dataclasses.replace(case, table=t)
+    for s in (1, 2, 0):
+        got = _run(pg, case, num_splits=s)
+        assert np.all(got[[0, 2, 3]] == 0)
+        ref = oracle.paged_gqa(**case.oracle_kwargs(), seq_ids=[1])
+        assert_parity(got[[1]], ref, f"empty rows splits {s}")
+
+
+def test_lengths_clamped_to_max_seq_len(pg):
+    case = inputs.decode_case(batch=2, lens=[100, 40], page_size=16, kv_dtype=FP16, seed=62)
+    clamped = dataclasses.replace(case, max_seq_len=64)
+    got = _run(pg, clamped)
+    ref = oracle.paged_gqa(**dataclasses.replace(
+        case, lens=np.minimum(case.lens, 64).astype(np.int32)).oracle_kwargs())
+    assert_parity(got, ref, "clamp")
+
+
+def test_bad_page_id_poisons_only_its_row(pg):
+    case = inputs.decode_case(batch=3, lens=[40, 40, 40], page_size=16, kv_dtype=E4M3, seed=63)
+    t = case.table.copy()
+    t[1, 1] = case.num_pages + 5
+    got = _run(pg, dataclasses.replace(case, table=t))
+    assert np.isnan(got[1]).all()
+    ref = oracle.paged_gqa(**case.oracle_kwargs(), seq_ids=[0, 2])
+    assert_parity(got[[0, 2]], ref, "rows next to a bad page id")
+
+
+# ------------------------------------------------------- bitwise invariants
+def test_page_permutation_bitwise(pg):
+    case = inputs.decode_case(batch=4, lens=[700, 333, 64, 1], page_size=16, kv_dtype=E4M3,
+                              seed=70, scales="uniform")
+    rng = np.random.default_rng(71)
+    perm = rng.permutation(case.num_pages)
+    ks = np.empty_like(case.k_store)
+    vs = np.empty_like(case.v_store)
+    ks[perm] = case.k_store
+    vs[perm] = case.v_store
+    moved = dataclasses.replace(case, k_store=ks, v_store=vs,
+                                table=perm[case.table].astype(np.int32))
+    for s in (1, 4):
+        assert np.array_equal(_run(pg, case, num_splits=s), _run(pg, moved, num_splits=s))
+
+
+@pytest.mark.parametrize("kv_dtype", [E4M3, FP16])
+def test_layouts_bitwise_equal(pg, kv_dtype):
+    outs = []
+    for layout in ("contiguous", "interleaved", "head_major"):
+        case = inputs.decode_case(batch=3, lens=[500, 77, 256], page_size=64, kv_dtype=kv_dtype,
+                                  layout=layout, seed=72, num_q_heads=12, num_kv_heads=2)
+        outs.append(_run(pg, case))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_deterministic_repeat(pg):
+    case = inputs.workload_case("decode_b8_1k_e4m3_p64")
+    a = _run(pg, case)
+    b = _run(pg, case)
+    assert np.array_equal(a, b)
+
+
+def test_prefill_equals_decode_bitwise(pg):
+    case = inputs.sparse_prefill_case(rows=32, selected_blocks=64, tail=2, pool_blocks=256,
+                                      seed=73)
+    for s in (1, 2):
+        a = _run(pg, case, prefill=True, num_splits=s)
+        b = _run(pg, case, prefill=False, num_splits=s)
+        assert np.array_equal(a, b)
+
+
+def test_graph_replay_bitwise(pg):
+    import torch
+
+    case = inputs.decode_case(batch=4, lens=[3000, 1500, 999, 4096], page_size=128,
+                              kv_dtype=E4M3, seed=74, scales="uniform")
+    q, pool, table, lens = pg.device_case(case)
+    n, hq, _ = q.shape
+    wsb = pg.paged_gqa_workspace_bytes(n, hq, 1, case.max_seq_len, 0)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    eager = torch.empty_like(q)
+    pg.paged_gqa_decode(q, pool, table, lens, case.max_seq_len, case.sm_scale, eager,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pg.paged_gqa_decode(q, pool, table, lens, case.max_seq_len, case.sm_scale, out,
+                            workspace=ws)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pg.paged_gqa_decode(q, pool, table, lens, case.max_seq_len, case.sm_scale, out,
+                            workspace=ws)
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
