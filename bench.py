@@ -9,7 +9,10 @@ so consecutive calls cannot be served from the 256 MB last-level cache.
 
 Prints ONE JSON line.  `value` is KV-read GB/s: algorithmic KV bytes per call
 (every live token's K and V row read once) divided by the average call time
-measured with HIP events on the stream the kernels run on.
+measured with HIP events on the stream the kernels run on.  `roofline` uses
+the dominant kernel alone (the attention kernel, timed the same way through
+paged_gqa_decode_partial with the same split plan); the whole call adds the
+split merge.
 """
 from __future__ import annotations
 
@@ -69,6 +72,46 @@ def cpu_baseline(case, budget_s: float) -> dict:
             "sample": f"{n_calls} whole calls of the same workload, {per_call * 1e3:.1f} ms each"}
 
 
+def time_steps(step, steps: int, warmup: int, R: int, use_graph: bool) -> float:
+    """Average milliseconds per step over exactly `steps` steps, timed with HIP
+    events on the stream the kernels run on.  With use_graph the R steps of
+    one pool rotation are captured once into a HIP graph and replayed (plus
+    steps % R eager steps), so Python's per-call overhead cannot leave the GPU
+    idle between steps."""
+    import torch
+
+    cur = torch.cuda.current_stream()
+    if use_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            for i in range(R):
+                step(i)
+        cur.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(R):
+                step(i)
+        rotation = graph.replay
+    else:
+        def rotation():
+            for i in range(R):
+                step(i)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for _ in range(steps // R):
+        rotation()
+    for i in range(steps % R):
+        step(i)
+    e1.record(cur)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -80,6 +123,8 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from Python instead of replaying a captured graph")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -113,26 +158,25 @@ def main() -> int:
                                          args.num_splits)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
     fn = pgqa.paged_gqa_prefill_sparse if prefill else pgqa.paged_gqa_decode
-    stream = torch.cuda.current_stream()
+    part_o = torch.empty((n, hq, splits, 256), dtype=torch.float32, device="cuda")
+    part_l = torch.empty((n, hq, splits), dtype=torch.float32, device="cuda")
 
-    def step(i):
+    def call(i):  # one whole call: attention (+ merge when split)
         fn(q, pools[i % R], table, lens, case.max_seq_len, case.sm_scale, out,
-           num_kv_heads=case.num_kv_heads, workspace=ws, num_splits=args.num_splits,
-           stream=stream)
+           num_kv_heads=case.num_kv_heads, workspace=ws, num_splits=args.num_splits)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    elapsed_ms = start.elapsed_time(end)
-    ms = elapsed_ms / args.steps
+    def attention_only(i):  # the dominant kernel alone, same launch configuration
+        pgqa.paged_gqa_decode_partial(q, pools[i % R], table, lens, case.max_seq_len,
+                                      case.sm_scale, part_o, part_l,
+                                      num_kv_heads=case.num_kv_heads,
+                                      num_splits=args.num_splits)
+
+    ms = time_steps(call, args.steps, args.warmup, R, not args.eager)
+    kernel_ms = ms if splits == 1 else time_steps(attention_only, args.steps, args.warmup, R,
+                                                  not args.eager)
     kv_bytes = case.kv_bytes_read()
     gbs = kv_bytes / (ms * 1e-3) / 1e9
+    kernel_gbs = kv_bytes / (kernel_ms * 1e-3) / 1e9
 
     src_hash = kernel_source_hash()
     traffic = measured_traffic(src_hash)
@@ -160,9 +204,10 @@ def main() -> int:
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "kernel_source_hash": src_hash,
         },
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "attention_kernel",
+                     "kernel_us": round(kernel_ms * 1e3, 3)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)

@@ -16,9 +16,23 @@
 
 namespace {
 
-using pgqa::kChunkAlign;
 using pgqa::kHeadDim;
 using pgqa::kMaxGroup;
+using pgqa::kTile;
+
+// Tuning constants (compile-time): waves per workgroup and resident waves
+// per compute unit the split plan aims for.
+#ifndef PGQA_WAVES_PER_WG
+#define PGQA_WAVES_PER_WG 4
+#endif
+#ifndef PGQA_WAVES_PER_CU
+#define PGQA_WAVES_PER_CU 8
+#endif
+constexpr int kWaves = PGQA_WAVES_PER_WG;
+// Upper bound on splits (the merge reads every partial of a head).
+constexpr int64_t kMaxSplits = 256;
+constexpr int kChunkAlign = kTile * kWaves;  // split length granularity
+static_assert(kWaves == 4 || kWaves == 8, "workgroups have 4 or 8 waves");
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
@@ -48,8 +62,8 @@ struct SplitPlan {
   int32_t chunk;
 };
 
-// Key-range splits: aim for two resident workgroups per compute unit, never
-// fewer than kChunkAlign tokens (one tile per wave) per split.
+// Key-range splits: aim for PGQA_WAVES_PER_CU resident waves per compute
+// unit, never fewer than kChunkAlign tokens (one tile per wave) per split.
 SplitPlan plan_splits(int64_t groups, int32_t max_len, int32_t requested, int cus) {
   const int64_t len = max_len > 0 ? max_len : 1;
   const int64_t max_splits = ceil_div(len, kChunkAlign);
@@ -57,13 +71,23 @@ SplitPlan plan_splits(int64_t groups, int32_t max_len, int32_t requested, int cu
   if (requested > 0) {
     s = requested;
   } else {
-    const int64_t target_wgs = 2LL * (cus > 0 ? cus : 256);
+    const int64_t target_wgs =
+        static_cast<int64_t>(cus > 0 ? cus : 256) * PGQA_WAVES_PER_CU / kWaves;
     s = ceil_div(target_wgs, groups > 0 ? groups : 1);
   }
   if (s > max_splits) s = max_splits;
+  if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
   const int64_t chunk = ceil_div(ceil_div(len, s), kChunkAlign) * kChunkAlign;
   return SplitPlan{static_cast<int32_t>(ceil_div(len, chunk)), static_cast<int32_t>(chunk)};
+}
+
+// Workspace: the fp32 split outputs [n*hq][splits][256], then their
+// log-sum-exps [n*hq][splits].
+size_t workspace_need(int32_t n, int32_t hq, int32_t hkv, int32_t splits) {
+  (void)hkv;
+  if (splits <= 1) return 0;
+  return static_cast<size_t>(n) * hq * splits * (kHeadDim + 1) * sizeof(float);
 }
 
 // Checks that need no HIP call.  Returns PGQA_OK or an error code.
@@ -106,26 +130,10 @@ int validate_call(const void* q, const pgqa_kv_pool* kv, const int32_t* table,
   return PGQA_OK;
 }
 
-int run_attention(const void* q, const pgqa_kv_pool* kv, const int32_t* table, int32_t max_pages,
-                  const int32_t* lens, int32_t max_len, int32_t n, int32_t hq, int32_t hkv,
-                  int32_t head_dim, float sm_scale, int32_t num_splits, void* out,
-                  void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = validate_call(q, kv, table, max_pages, lens, max_len, n, hq, hkv, head_dim, sm_scale,
-                         num_splits, out);
-  if (rc != PGQA_OK || n == 0) return rc;
-
-  int cus = 0;
-  if (num_splits == 0) {
-    cus = current_cu_count();
-    if (cus <= 0) return PGQA_ERR_HIP;
-  }
-  const SplitPlan plan = plan_splits(static_cast<int64_t>(n) * hkv, max_len, num_splits, cus);
-  const size_t need =
-      plan.splits > 1 ? static_cast<size_t>(n) * hq * plan.splits * (kHeadDim + 1) * sizeof(float)
-                      : 0;
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
-    return PGQA_ERR_WORKSPACE;
-
+// Fills the launch parameters shared by every attention call.
+pgqa::AttnParams make_params(const void* q, const pgqa_kv_pool* kv, const int32_t* table,
+                             int32_t max_pages, const int32_t* lens, int32_t max_len, int32_t n,
+                             int32_t hq, int32_t hkv, float sm_scale, const SplitPlan& plan) {
   const bool fp8 = kv->kv_dtype == PGQA_KV_E4M3;
   const int64_t es = fp8 ? 1 : 2;
   pgqa::AttnParams p{};
@@ -152,13 +160,49 @@ int run_attention(const void* q, const pgqa_kv_pool* kv, const int32_t* table, i
   p.v_scale = fp8 ? kv->v_scale : 1.0f;
   p.splits = plan.splits;
   p.chunk = plan.chunk;
+  p.waves = kWaves;
+  return p;
+}
+
+// The split plan of a validated call (queries the device only for num_splits = 0).
+int plan_call(int32_t n, int32_t hkv, int32_t max_len, int32_t num_splits, SplitPlan* plan) {
+  int cus = 0;
+  if (num_splits == 0) {
+    cus = current_cu_count();
+    if (cus <= 0) return PGQA_ERR_HIP;
+  }
+  *plan = plan_splits(static_cast<int64_t>(n) * hkv, max_len, num_splits, cus);
+  return PGQA_OK;
+}
+
+int run_attention(const void* q, const pgqa_kv_pool* kv, const int32_t* table, int32_t max_pages,
+                  const int32_t* lens, int32_t max_len, int32_t n, int32_t hq, int32_t hkv,
+                  int32_t head_dim, float sm_scale, int32_t num_splits, void* out,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_call(q, kv, table, max_pages, lens, max_len, n, hq, hkv, head_dim, sm_scale,
+                         num_splits, out);
+  if (rc != PGQA_OK || n == 0) return rc;
+  SplitPlan plan;
+  rc = plan_call(n, hkv, max_len, num_splits, &plan);
+  if (rc != PGQA_OK) return rc;
+  const size_t need = workspace_need(n, hq, hkv, plan.splits);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return PGQA_ERR_WORKSPACE;
+
+  const bool fp8 = kv->kv_dtype == PGQA_KV_E4M3;
+  pgqa::AttnParams p = make_params(q, kv, table, max_pages, lens, max_len, n, hq, hkv, sm_scale,
+                                   plan);
   p.out = static_cast<uint16_t*>(out);
-  if (plan.splits > 1) {
+  p.partials = plan.splits > 1;
+  if (p.partials) {
     p.ws_o = static_cast<float*>(workspace);
     p.ws_lse = p.ws_o + static_cast<size_t>(n) * hq * plan.splits * kHeadDim;
   }
-  hipError_t err = pgqa::launch_attention(p, fp8, static_cast<hipStream_t>(stream));
-  return err == hipSuccess ? PGQA_OK : PGQA_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pgqa::launch_attention(p, fp8, s) != hipSuccess) return PGQA_ERR_HIP;
+  if (!p.partials) return PGQA_OK;
+  pgqa::MergeParams m{p.ws_o, p.ws_lse, static_cast<int64_t>(n) * hq, plan.splits, p.out};
+  return pgqa::launch_merge(m, s) == hipSuccess ? PGQA_OK : PGQA_ERR_HIP;
 }
 
 }  // namespace
@@ -184,8 +228,7 @@ size_t paged_gqa_workspace_bytes(int32_t n, int32_t num_q_heads, int32_t num_kv_
     return SIZE_MAX;
   const int32_t splits = paged_gqa_num_splits(n, num_kv_heads, max_seq_len, num_splits);
   if (splits < 1) return SIZE_MAX;
-  if (splits == 1) return 0;
-  return static_cast<size_t>(n) * num_q_heads * splits * (kHeadDim + 1) * sizeof(float);
+  return workspace_need(n, num_q_heads, num_kv_heads, splits);
 }
 
 int paged_gqa_decode(const void* q, const pgqa_kv_pool* kv, const int32_t* page_table,
@@ -206,6 +249,42 @@ int paged_gqa_prefill_sparse(const void* q, const pgqa_kv_pool* kv, const int32_
   return run_attention(q, kv, row_tables, max_pages, row_lens, max_row_len, rows, num_q_heads,
                        num_kv_heads, head_dim, sm_scale, num_splits, out, workspace,
                        workspace_bytes, stream);
+}
+
+int paged_gqa_decode_partial(const void* q, const pgqa_kv_pool* kv, const int32_t* page_table,
+                             int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len,
+                             int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, float sm_scale, int32_t num_splits,
+                             float* part_o, float* part_lse, void* stream) {
+  // `out` is not written here; pass part_o to the shared checks in its place.
+  int rc = validate_call(q, kv, page_table, max_pages, seq_lens, max_seq_len, batch, num_q_heads,
+                         num_kv_heads, head_dim, sm_scale, num_splits, part_o);
+  if (rc != PGQA_OK || batch == 0) return rc;
+  if (!part_lse) return PGQA_ERR_NULL;
+  if (!aligned16(part_lse)) return PGQA_ERR_LAYOUT;
+  SplitPlan plan;
+  rc = plan_call(batch, num_kv_heads, max_seq_len, num_splits, &plan);
+  if (rc != PGQA_OK) return rc;
+  pgqa::AttnParams p = make_params(q, kv, page_table, max_pages, seq_lens, max_seq_len, batch,
+                                   num_q_heads, num_kv_heads, sm_scale, plan);
+  p.partials = true;
+  p.ws_o = part_o;
+  p.ws_lse = part_lse;
+  return pgqa::launch_attention(p, kv->kv_dtype == PGQA_KV_E4M3,
+                                static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PGQA_OK
+             : PGQA_ERR_HIP;
+}
+
+int paged_gqa_merge_partials(const float* part_o, const float* part_lse, int32_t rows,
+                             int32_t splits, int32_t head_dim, void* out, void* stream) {
+  if (head_dim != kHeadDim || rows < 0 || splits < 1) return PGQA_ERR_SHAPE;
+  if (rows == 0) return PGQA_OK;
+  if (!part_o || !part_lse || !out) return PGQA_ERR_NULL;
+  if (!aligned16(part_o) || !aligned16(out)) return PGQA_ERR_LAYOUT;
+  pgqa::MergeParams m{part_o, part_lse, rows, splits, static_cast<uint16_t*>(out)};
+  return pgqa::launch_merge(m, static_cast<hipStream_t>(stream)) == hipSuccess ? PGQA_OK
+                                                                                : PGQA_ERR_HIP;
 }
 
 int e4m3_decode_table(float* out256, void* stream) {

@@ -9,9 +9,7 @@ namespace pgqa {
 
 constexpr int kHeadDim = 256;   // head dimension the kernels are built for
 constexpr int kTile = 16;       // tokens per wave tile (one MFMA M/K block)
-constexpr int kWaves = 4;       // waves per workgroup, each on its own tiles
-constexpr int kThreads = 64 * kWaves;
-constexpr int kChunkAlign = kTile * kWaves;  // split length granularity
+constexpr int kMaxWaves = 8;    // waves per workgroup (4 or 8), each on its own tiles
 constexpr int kMaxGroup = 16;   // query heads per kv head (MFMA N = 16)
 
 // Everything a launch needs; strides already converted to bytes.
@@ -36,14 +34,26 @@ struct AttnParams {
   float qk_scale_log2;     // sm_scale * k_scale * log2(e) (k_scale = 1 for FP16)
   float v_scale;           // 1 for FP16
   int32_t splits;          // key-range splits per (sequence, kv head)
-  int32_t chunk;           // tokens per split, multiple of kChunkAlign
+  int32_t chunk;           // tokens per split, multiple of kTile * waves
+  int32_t waves;           // waves per workgroup: 4 or 8
+  bool partials;           // write split partials (ws_o, ws_lse) instead of out
   uint16_t* out;           // fp16 bits [n][hq][256]
-  float* ws_o;             // [n*hq][splits][256] normalised split outputs
-  float* ws_lse;           // [n*hq][splits] log2-domain log-sum-exp
+  float* ws_o;             // [n*hq][splits][256] split outputs (v_scale applied)
+  float* ws_lse;           // [n*hq][splits] base-2 log-sum-exp, -inf if empty
+};
+
+// Merge of split partials into fp16 rows.
+struct MergeParams {
+  const float* o;          // [rows][splits][256]
+  const float* lse;        // [rows][splits]
+  int64_t rows;
+  int32_t splits;
+  uint16_t* out;           // fp16 bits [rows][256]
 };
 
 hipError_t launch_attention(const AttnParams& p, bool fp8, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_e4m3_table(float* out256, hipStream_t stream);
-size_t attention_lds_bytes(int group);
+size_t attention_lds_bytes(int group, int waves);
 
 }  // namespace pgqa

@@ -11,12 +11,15 @@
 //     clamped to their live length, invalid rows inert, page ids of a tile
 //     staged ahead of its loads.
 //
-// Work decomposition.  One workgroup of four waves owns one (sequence or row
+// Work decomposition.  One workgroup of NW (4 or 8) waves owns one (sequence or row
 // b, kv head g, split s): the tokens [s*chunk, min((s+1)*chunk, L_b)).  Wave
 // w takes the 16-token tiles w, w+4, w+8, ... of that range and keeps its own
 // online-softmax state; the four states are merged through LDS at the end.
 // With one split the workgroup writes the fp16 output; with several it writes
-// a normalised fp32 partial and its log2-sum-exp, merged by combine_kernel.
+// a normalised fp32 partial and its base-2 log-sum-exp, merged by merge_kernel
+// in a second launch (a kernel boundary makes the partials visible; fencing
+// them from inside the first kernel writes back the whole L2 of an XCD per
+// workgroup and costs far more).
 //
 // Per tile (lane = 16*qd + r, r = lane % 16, qd = lane / 16):
 //   QK^T on MFMA 16x16x32 f16: M = the 16 tokens (A = K rows, lane r holds
@@ -115,7 +118,7 @@ struct TileRegs {
   u4_t v[4][Geo<FP8>::kV];
 };
 
-template <bool FP8>
+template <bool FP8, int NW>
 struct Wave {
   // constant per wave
   const AttnParams& p;
@@ -129,7 +132,7 @@ struct Wave {
   bool bad;
 
   __device__ __forceinline__ int tile_start(int k) const {
-    return s0 + (wave + kWaves * k) * kTile;
+    return s0 + (wave + NW * k) * kTile;
   }
 
   // Page id (table entry) for this lane's K token of tile k; slot returned.
@@ -252,8 +255,9 @@ struct Wave {
   }
 };
 
-template <bool FP8>
-__global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
+template <bool FP8, int NW>
+__global__ __launch_bounds__(64 * NW) void attention_kernel(AttnParams p) {
+  constexpr int kNT = 64 * NW;
   extern __shared__ float smem[];
   const int lane = threadIdx.x & 63;
   // The wave index is uniform across the wave; saying so keeps the tile loop
@@ -268,9 +272,16 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
   const int L = min(p.lens[b], p.max_len);
   const int s0 = split * p.chunk;
   const int s1 = min(s0 + p.chunk, L);
-  if (p.splits > 1 && s0 >= L) return;  // split past the end: nothing to merge
+  if (p.partials && s0 >= L) {
+    // A split with no live token: its partial is empty (lse = -inf).
+    if (threadIdx.x < p.group) {
+      const int64_t oh = static_cast<int64_t>(b) * p.hq + g * p.group + threadIdx.x;
+      p.ws_lse[oh * p.splits + split] = -__builtin_huge_valf();
+    }
+    return;
+  }
 
-  Wave<FP8> W{p};
+  Wave<FP8, NW> W{p};
   W.tab = p.table + static_cast<int64_t>(b) * p.max_pages;
   W.head_off = static_cast<int64_t>(g) * p.head_stride;
   W.s0 = s0;
@@ -300,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
   }
 
   const int span = s1 - s0 - wave * kTile;
-  const int ntiles = span > 0 ? (span + kWaves * kTile - 1) / (kWaves * kTile) : 0;
+  const int ntiles = span > 0 ? (span + NW * kTile - 1) / (NW * kTile) : 0;
 
   // Software pipeline: while tile k is computed, tile k+1's K/V loads and
   // tile k+2's page-table entries are in flight.  The page-table load of tile
@@ -338,12 +349,12 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
     }
   }
 
-  // ---- merge the four waves through LDS
+  // ---- merge the waves of the workgroup through LDS
   const int group = p.group;
-  float* so = smem;                               // [kWaves][group][kLdsRow]
-  float* sm = so + kWaves * group * kLdsRow;      // [kWaves][16]
-  float* sl = sm + kWaves * 16;                   // [kWaves][16]
-  int* sbad = reinterpret_cast<int*>(sl + kWaves * 16);  // [kWaves]
+  float* so = smem;                           // [NW][group][kLdsRow]
+  float* sm = so + NW * group * kLdsRow;      // [NW][16]
+  float* sl = sm + NW * 16;                   // [NW][16]
+  int* sflags = reinterpret_cast<int*>(sl + NW * 16);  // [NW] bad-page flags
   float l_tot = W.l_run + __shfl_xor(W.l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   const bool wave_bad = __ballot(W.bad) != 0;
@@ -359,18 +370,21 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
       sl[wave * 16 + W.r] = l_tot;
     }
   }
-  if (lane == 0) sbad[wave] = wave_bad ? 1 : 0;
+  if (lane == 0) sflags[wave] = wave_bad ? 1 : 0;
   __syncthreads();
 
-  const int d = threadIdx.x;  // kThreads == kHeadDim
-  const bool any_bad = (sbad[0] | sbad[1] | sbad[2] | sbad[3]) != 0;
-  for (int h = 0; h < group; ++h) {
+  bool any_bad = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) any_bad |= sflags[w] != 0;
+  for (int idx = threadIdx.x; idx < group * kHeadDim; idx += kNT) {
+    const int h = idx >> 8;
+    const int d = idx & (kHeadDim - 1);
     float M = -__builtin_huge_valf();
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * 16 + h]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w * 16 + h]);
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float mw = sm[w * 16 + h];
       if (mw != -__builtin_huge_valf()) {
         const float e = __builtin_amdgcn_exp2f(mw - M);
@@ -379,41 +393,77 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
       }
     }
     const int64_t oh = static_cast<int64_t>(b) * p.hq + g * group + h;
-    if (p.splits == 1) {
+    if (!p.partials) {
       float o = den > 0.f ? (num / den) * p.v_scale : 0.f;
       if (any_bad) o = __builtin_nanf("");
       p.out[oh * kHeadDim + d] = f16_bits(o);
     } else {
-      float o = num / den;
+      // With partials the split has a live token (or the sequence is empty
+      // and den = 0, lse = -inf).
+      float o = den > 0.f ? (num / den) * p.v_scale : 0.f;
       if (any_bad) o = __builtin_nanf("");
       p.ws_o[(oh * p.splits + split) * kHeadDim + d] = o;
-      if (d == 0) p.ws_lse[oh * p.splits + split] = M + __log2f(den);
+      if (d == 0) p.ws_lse[oh * p.splits + split] = den > 0.f ? M + __log2f(den)
+                                                             : -__builtin_huge_valf();
     }
   }
 }
 
-// Merge the split partials of one (sequence, query head): weights 2^(lse_s - max).
-__global__ __launch_bounds__(kHeadDim) void combine_kernel(AttnParams p) {
-  const int oh = blockIdx.x;
-  const int b = oh / p.hq;
-  const int d = threadIdx.x;
-  const int L = min(p.lens[b], p.max_len);
-  const int nact = L > 0 ? (L + p.chunk - 1) / p.chunk : 0;
-  float o = 0.f;
-  if (nact > 0) {
-    const float* lse = p.ws_lse + static_cast<int64_t>(oh) * p.splits;
-    float M = -__builtin_huge_valf();
-    for (int s = 0; s < nact; ++s) M = fmaxf(M, lse[s]);
-    float num = 0.f, den = 0.f;
-    const float* po = p.ws_o + static_cast<int64_t>(oh) * p.splits * kHeadDim + d;
-    for (int s = 0; s < nact; ++s) {
-      const float e = __builtin_amdgcn_exp2f(lse[s] - M);
-      num += e * po[static_cast<int64_t>(s) * kHeadDim];
-      den += e;
+// Merge the split partials of one (row, query head): one wave, each lane
+// owning 4 consecutive head dims.  Split s is weighted by 2^(lse_s - max lse);
+// a split with lse = -inf (no live token) has weight 0 and its stored output
+// is not used.  The lse values and the partial outputs of a chunk of 32
+// splits are loaded together, so a chunk costs about one memory round trip.
+__global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
+  constexpr int kChunk = 32;
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* lse = p.lse + row * p.splits;
+  const float4* po =
+      reinterpret_cast<const float4*>(p.o + row * p.splits * kHeadDim) + lane;
+  float M = -__builtin_huge_valf(), den = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < p.splits; c0 += kChunk) {
+    float4 v[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      v[u] = (c0 + u < p.splits) ? po[static_cast<int64_t>(c0 + u) * (kHeadDim / 4)]
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float l = (lane < kChunk && c0 + lane < p.splits) ? lse[c0 + lane]
+                                                           : -__builtin_huge_valf();
+    float mc = l;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mc = fmaxf(mc, __shfl_xor(mc, o));
+    const float m_new = fmaxf(M, mc);
+    if (m_new == -__builtin_huge_valf()) continue;  // nothing live so far
+    const float alpha = __builtin_amdgcn_exp2f(M - m_new);  // 0 when M = -inf
+    const float wl = l == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(l - m_new);
+    float ws = wl;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
+    den = den * alpha + ws;
+    acc.x *= alpha;
+    acc.y *= alpha;
+    acc.z *= alpha;
+    acc.w *= alpha;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
+      if (w != 0.f) {
+        acc.x += w * v[u].x;
+        acc.y += w * v[u].y;
+        acc.z += w * v[u].z;
+        acc.w += w * v[u].w;
+      }
     }
-    o = (num / den) * p.v_scale;
+    M = m_new;
   }
-  p.out[static_cast<int64_t>(oh) * kHeadDim + d] = f16_bits(o);
+  const float scale = den > 0.f ? 1.f / den : 0.f;
+  uint16_t* op = p.out + row * kHeadDim + 4 * lane;
+  u2_t packed;
+  packed[0] = f16_bits(acc.x * scale) | (static_cast<uint32_t>(f16_bits(acc.y * scale)) << 16);
+  packed[1] = f16_bits(acc.z * scale) | (static_cast<uint32_t>(f16_bits(acc.w * scale)) << 16);
+  *reinterpret_cast<u2_t*>(op) = packed;
 }
 
 __global__ void e4m3_table_kernel(float* out) {
@@ -422,44 +472,40 @@ __global__ void e4m3_table_kernel(float* out) {
   out[c] = static_cast<float>(__builtin_bit_cast(h2_t, h)[0]);
 }
 
-}  // namespace
-
-size_t attention_lds_bytes(int group) {
-  return sizeof(float) * (static_cast<size_t>(kWaves) * group * kLdsRow + 2 * kWaves * 16) +
-         sizeof(int) * kWaves;
+template <bool FP8, int NW>
+hipError_t launch(const AttnParams& p, hipStream_t stream) {
+  const size_t lds = attention_lds_bytes(p.group, NW);
+  if (lds > 65536) {
+    // Merge buffers beyond the default 64 KiB dynamic LDS limit need the
+    // limit raised (once per process and kernel).
+    static const hipError_t raised = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(attention_kernel<FP8, NW>),
+        hipFuncAttributeMaxDynamicSharedMemorySize,
+        static_cast<int>(attention_lds_bytes(kMaxGroup, NW)));
+    if (raised != hipSuccess) return raised;
+  }
+  const dim3 grid(static_cast<unsigned>(p.splits) * p.n * p.hkv);
+  hipLaunchKernelGGL((attention_kernel<FP8, NW>), grid, dim3(64 * NW), lds, stream, p);
+  return hipGetLastError();
 }
 
-// Kernels whose merge buffer exceeds the default 64 KiB dynamic LDS limit
-// (groups of more than 12 heads) need the limit raised once per process.
-static hipError_t allow_large_lds() {
-  static hipError_t status = [] {
-    const int bytes = static_cast<int>(attention_lds_bytes(kMaxGroup));
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attention_kernel<true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(attention_kernel<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    return e;
-  }();
-  return status;
+}  // namespace
+
+size_t attention_lds_bytes(int group, int waves) {
+  return sizeof(float) * (static_cast<size_t>(waves) * group * kLdsRow + 2 * waves * 16) +
+         sizeof(int) * waves;
 }
 
 hipError_t launch_attention(const AttnParams& p, bool fp8, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(p.splits) * p.n * p.hkv);
-  const size_t lds = attention_lds_bytes(p.group);
-  if (lds > 65536) {
-    hipError_t e = allow_large_lds();
-    if (e != hipSuccess) return e;
+  switch (p.waves) {
+    case 4: return fp8 ? launch<true, 4>(p, stream) : launch<false, 4>(p, stream);
+    case 8: return fp8 ? launch<true, 8>(p, stream) : launch<false, 8>(p, stream);
+    default: return hipErrorInvalidValue;
   }
-  if (fp8) {
-    hipLaunchKernelGGL(attention_kernel<true>, grid, dim3(kThreads), lds, stream, p);
-  } else {
-    hipLaunchKernelGGL(attention_kernel<false>, grid, dim3(kThreads), lds, stream, p);
-  }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || p.splits == 1) return err;
-  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(p.n) * p.hq), dim3(kHeadDim), 0,
-                     stream, p);
+}
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(p.rows)), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -29,7 +29,8 @@ SIZE_MAX = ctypes.c_size_t(-1).value
 
 # Every symbol include/pgqa.h declares.
 EXPORTS = ("paged_gqa_workspace_bytes", "paged_gqa_num_splits", "paged_gqa_decode",
-           "paged_gqa_prefill_sparse", "e4m3_decode_table", "pgqa_error_string")
+           "paged_gqa_prefill_sparse", "paged_gqa_decode_partial", "paged_gqa_merge_partials",
+           "e4m3_decode_table", "pgqa_error_string")
 
 
 class PgqaError(RuntimeError):
@@ -73,6 +74,11 @@ def _lib(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = attn_args
+    lib.paged_gqa_decode_partial.restype = ctypes.c_int
+    lib.paged_gqa_decode_partial.argtypes = [vp, ctypes.POINTER(KVPoolC), vp, i32, vp, i32, i32,
+                                             i32, i32, i32, f32, i32, vp, vp, vp]
+    lib.paged_gqa_merge_partials.restype = ctypes.c_int
+    lib.paged_gqa_merge_partials.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.e4m3_decode_table.restype = ctypes.c_int
     lib.e4m3_decode_table.argtypes = [vp, vp]
     lib.pgqa_error_string.restype = ctypes.c_char_p
@@ -170,6 +176,31 @@ def _call(fn_name, q, kv, table, lens, max_len, hkv, sm_scale, num_splits, out, 
         int(max_len), int(n), int(hq), int(hkv), int(d), float(sm_scale), int(num_splits),
         _ptr(out), _ptr(workspace), int(ws_bytes), _stream_handle(stream))
     _check(rc, fn_name)
+
+
+def paged_gqa_decode_partial(q, kv: KVPool, page_table, seq_lens, max_seq_len: int,
+                             sm_scale: float, part_o, part_lse, num_kv_heads: int = 1,
+                             num_splits: int = 0, stream=None) -> None:
+    """part_o: fp32 [B][Hq][S][256]; part_lse: fp32 [B][Hq][S] with
+    S = paged_gqa_num_splits(B, num_kv_heads, max_seq_len, num_splits)."""
+    n, hq, d = q.shape
+    c_pool = kv.as_c()
+    rc = _lib().paged_gqa_decode_partial(
+        _ptr(q), ctypes.byref(c_pool), _ptr(page_table), int(page_table.shape[1]),
+        _ptr(seq_lens), int(max_seq_len), int(n), int(hq), int(num_kv_heads), int(d),
+        float(sm_scale), int(num_splits), _ptr(part_o), _ptr(part_lse), _stream_handle(stream))
+    _check(rc, "paged_gqa_decode_partial")
+
+
+def paged_gqa_merge_partials(part_o, part_lse, out, stream=None) -> None:
+    """part_o: fp32 [rows][S][256]; part_lse: fp32 [rows][S]; out: fp16 [rows][256]
+    (any leading shape that flattens to these)."""
+    splits = part_lse.shape[-1]
+    rows = part_lse.numel() // splits
+    rc = _lib().paged_gqa_merge_partials(_ptr(part_o), _ptr(part_lse), int(rows), int(splits),
+                                         int(part_o.shape[-1]), _ptr(out),
+                                         _stream_handle(stream))
+    _check(rc, "paged_gqa_merge_partials")
 
 
 def e4m3_decode_table(out, stream=None) -> None:

@@ -91,7 +91,8 @@ typedef struct pgqa_kv_pool {
  * `num_q_heads` heads and `max_seq_len`, with `num_splits` (0 = the automatic
  * choice for the current device).  Returns 0 when no workspace is needed
  * (a single split) and SIZE_MAX on invalid arguments or a HIP query failure.
- * The workspace holds split partials only; it needs no initialisation.
+ * The workspace holds the fp32 split partials only; it needs no
+ * initialisation.
  */
 size_t paged_gqa_workspace_bytes(int32_t n, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_seq_len, int32_t num_splits);
@@ -120,14 +121,17 @@ int32_t paged_gqa_num_splits(int32_t n, int32_t num_kv_heads, int32_t max_seq_le
  * num_q_heads: group * num_kv_heads with 1 <= group <= 16 (6 in the pages).
  * head_dim   : must be 256.
  * sm_scale   : softmax scale applied to q.K (finite).
- * num_splits : number of key-range splits per (sequence, kv head), 0 = auto.
- *              More than one split writes per-split partials to `workspace`
- *              and a second kernel merges them with their log-sum-exp.
+ * num_splits : number of key-range splits per (sequence, kv head), 0 = auto;
+ *              capped at 256 and at one split per 64 tokens (query the
+ *              effective count with paged_gqa_num_splits).
+ *              With more than one split the call runs as
+ *              paged_gqa_decode_partial into `workspace` followed by
+ *              paged_gqa_merge_partials, both enqueued on `stream`.
  * out        : fp16 [batch][num_q_heads][256], contiguous, 16-byte aligned;
  *              must not alias q.
  * workspace  : device scratch of at least paged_gqa_workspace_bytes(...) bytes
- *              (may be NULL when that is 0), 16-byte aligned, not shared with
- *              a concurrently running call.
+ *              (may be NULL when that is 0), 16-byte aligned, not shared
+ *              with a concurrently running call.
  */
 int paged_gqa_decode(const void* q, const pgqa_kv_pool* kv, const int32_t* page_table,
                      int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len,
@@ -153,6 +157,39 @@ int paged_gqa_prefill_sparse(const void* q, const pgqa_kv_pool* kv, const int32_
                              int32_t rows, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t head_dim, float sm_scale, int32_t num_splits, void* out,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * First stage of paged_gqa_decode alone: per-split partial results, for
+ * callers that merge them themselves (e.g. shards of one sequence computed on
+ * different devices).  Same arguments as paged_gqa_decode up to num_splits.
+ * With S = paged_gqa_num_splits(batch, num_kv_heads, max_seq_len, num_splits),
+ * split s of sequence b covers the tokens [s*C, min((s+1)*C, L_b)) for a
+ * chunk C = ceil(max_seq_len / S) rounded up to a multiple of 64, and writes
+ *   part_o  : fp32 [batch][num_q_heads][S][256], 16-byte aligned: the
+ *             split's softmax-weighted mean of V (v_scale applied);
+ *   part_lse: fp32 [batch][num_q_heads][S]: log2(sum_t exp(z_t)) over the
+ *             split's tokens, or -inf for a split with no live token (its
+ *             part_o is then not written).
+ * Both buffers are caller-allocated device memory of at least the sizes above.
+ */
+int paged_gqa_decode_partial(const void* q, const pgqa_kv_pool* kv, const int32_t* page_table,
+                             int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len,
+                             int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, float sm_scale, int32_t num_splits,
+                             float* part_o, float* part_lse, void* stream);
+
+/*
+ * Second stage: merge `splits` partials per row by their log-sum-exp
+ * (source: "[Kernel][SM70] Scale NVFP4 E4M3 decode batches", Purpose -- the
+ * long-context decode routes).  For each of `rows` rows (a row is one
+ * (sequence, query head)): out[r] = sum_s 2^(lse_s - M) o_s / sum_s
+ * 2^(lse_s - M), M = max_s lse_s; splits with lse = -inf are skipped and a
+ * row whose splits are all -inf is zero.  part_o fp32 [rows][splits][256]
+ * and out fp16 [rows][256] are 16-byte aligned; part_lse is fp32
+ * [rows][splits]; head_dim must be 256.
+ */
+int paged_gqa_merge_partials(const float* part_o, const float* part_lse, int32_t rows,
+                             int32_t splits, int32_t head_dim, void* out, void* stream);
 
 /*
  * Writes to out256[c] (device, fp32 [256]) the value the attention kernels'

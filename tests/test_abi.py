@@ -127,7 +127,29 @@ def test_workspace_bytes(lib):
     assert lib.paged_gqa_num_splits(1, 1, 16384, 32) == 32
     assert lib.paged_gqa_num_splits(1, 1, 16384, 7) == 7
     assert lib.paged_gqa_num_splits(1, 1, 0, 3) == 1
+    assert lib.paged_gqa_num_splits(1, 1, 1 << 22, 100000) == 256
     assert lib.paged_gqa_num_splits(1, 0, 10, 3) < 0
+
+
+def test_partial_and_merge_validation(lib):
+    E = pgqa
+    kv = pool()
+    args = lambda **kw: [kw.get("q", FAKE), ctypes.byref(kw.get("kv", kv)), FAKE, 64, FAKE,  # noqa: E731
+                         1024, 2, 6, 1, kw.get("d", 256), 0.0625, 4, kw.get("po", FAKE * 4),
+                         kw.get("pl", FAKE * 8), None]
+    assert lib.paged_gqa_decode_partial(*args(q=None)) == E.PGQA_ERR_NULL
+    assert lib.paged_gqa_decode_partial(*args(po=None)) == E.PGQA_ERR_NULL
+    assert lib.paged_gqa_decode_partial(*args(pl=None)) == E.PGQA_ERR_NULL
+    assert lib.paged_gqa_decode_partial(*args(pl=FAKE * 8 + 4)) == E.PGQA_ERR_LAYOUT
+    assert lib.paged_gqa_decode_partial(*args(d=64)) == E.PGQA_ERR_SHAPE
+    m = lib.paged_gqa_merge_partials
+    assert m(FAKE, FAKE, 10, 4, 128, FAKE, None) == E.PGQA_ERR_SHAPE
+    assert m(FAKE, FAKE, 10, 0, 256, FAKE, None) == E.PGQA_ERR_SHAPE
+    assert m(FAKE, FAKE, -1, 4, 256, FAKE, None) == E.PGQA_ERR_SHAPE
+    assert m(None, FAKE, 10, 4, 256, FAKE, None) == E.PGQA_ERR_NULL
+    assert m(FAKE, FAKE, 10, 4, 256, None, None) == E.PGQA_ERR_NULL
+    assert m(FAKE + 8, FAKE, 10, 4, 256, FAKE, None) == E.PGQA_ERR_LAYOUT
+    assert m(None, None, 0, 4, 256, None, None) == E.PGQA_OK  # nothing to do
 
 
 def test_e4m3_table_rejects_null(lib):

@@ -225,6 +225,102 @@ def test_prefill_equals_decode_bitwise(pg):
         assert np.array_equal(a, b)
 
 
+def test_reused_workspace_and_empty_rows(pg):
+    import torch
+
+    case = inputs.decode_case(batch=5, lens=[3000, 0, 1, 2049, 64], page_size=64, kv_dtype=E4M3,
+                              seed=75, scales="uniform")
+    q, pool, table, lens = pg.device_case(case)
+    n, hq, _ = q.shape
+    wsb = pg.paged_gqa_workspace_bytes(n, hq, 1, case.max_seq_len, 6)
+    ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device="cuda")  # garbage, not zero
+    outs = []
+    for _ in range(3):
+        out = torch.full_like(q, float("nan"))
+        pg.paged_gqa_decode(q, pool, table, lens, case.max_seq_len, case.sm_scale, out,
+                            workspace=ws, num_splits=6)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    assert np.all(outs[0][1] == 0)
+    ref = oracle.paged_gqa(**case.oracle_kwargs())
+    assert_parity(outs[0], ref, "reused workspace")
+
+
+@pytest.mark.parametrize("splits", [2, 5, 0])
+def test_partial_then_merge_equals_decode_bitwise(pg, splits):
+    import torch
+
+    case = inputs.decode_case(batch=3, lens=[4000, 1, 2500], page_size=128, kv_dtype=E4M3,
+                              seed=76, scales="uniform")
+    q, pool, table, lens = pg.device_case(case)
+    n, hq, _ = q.shape
+    S = pg.paged_gqa_num_splits(n, 1, case.max_seq_len, splits)
+    po = torch.empty((n, hq, S, 256), dtype=torch.float32, device="cuda")
+    pl = torch.empty((n, hq, S), dtype=torch.float32, device="cuda")
+    pg.paged_gqa_decode_partial(q, pool, table, lens, case.max_seq_len, case.sm_scale, po, pl,
+                                num_splits=splits)
+    merged = torch.empty_like(q)
+    pg.paged_gqa_merge_partials(po, pl, merged)
+    direct = pg.run_case(case, num_splits=splits)
+    torch.cuda.synchronize()
+    if S > 1:
+        assert torch.equal(merged, direct)
+    # Splits past a sequence's end are marked empty.
+    lse = pl.cpu().numpy()
+    assert np.all(np.isneginf(lse[1, :, 1:]))
+    assert np.all(np.isfinite(lse[1, :, 0]))
+
+
+def test_merge_of_shards_equals_whole_sequence(pg):
+    """Two shards of each sequence's pages computed separately (one split
+    each) and merged by paged_gqa_merge_partials equal attention over the
+    whole sequence -- the merge a context-parallel split would use."""
+    import torch
+
+    case = inputs.decode_case(batch=4, lens=[2048, 1000, 64, 1536], page_size=64,
+                              kv_dtype=E4M3, seed=77, scales="uniform")
+    ref = oracle.paged_gqa(**case.oracle_kwargs())
+    n = case.n
+    cut = np.array([640, 512, 64, 1536])   # shard boundary (multiple of the page size)
+    lens_a = np.minimum(case.lens, cut).astype(np.int32)
+    lens_b = (case.lens - lens_a).astype(np.int32)
+    tab_b = np.zeros_like(case.table)
+    for b in range(n):
+        k = cut[b] // 64
+        tab_b[b, :case.table.shape[1] - k] = case.table[b, k:]
+    q, pool, table, _ = pg.device_case(case)
+    hq = q.shape[1]
+    parts_o = torch.empty((n, hq, 2, 256), dtype=torch.float32, device="cuda")
+    parts_l = torch.empty((n, hq, 2), dtype=torch.float32, device="cuda")
+    for j, (tab, ln) in enumerate([(case.table, lens_a), (tab_b, lens_b)]):
+        po = torch.empty((n, hq, 1, 256), dtype=torch.float32, device="cuda")
+        pl = torch.empty((n, hq, 1), dtype=torch.float32, device="cuda")
+        pg.paged_gqa_decode_partial(q, pool, torch.from_numpy(tab).cuda(),
+                                    torch.from_numpy(ln).cuda(), case.max_seq_len,
+                                    case.sm_scale, po, pl, num_splits=1)
+        parts_o[:, :, j] = po[:, :, 0]
+        parts_l[:, :, j] = pl[:, :, 0]
+    out = torch.empty_like(q)
+    pg.paged_gqa_merge_partials(parts_o, parts_l, out)
+    torch.cuda.synchronize()
+    assert_parity(out.cpu().numpy(), ref, "merged shards")
+
+
+def test_merge_all_empty_rows_are_zero(pg):
+    import torch
+
+    po = torch.full((3, 4, 256), float("nan"), dtype=torch.float32, device="cuda")
+    pl = torch.full((3, 4), float("-inf"), dtype=torch.float32, device="cuda")
+    pl[1, 2] = 0.5
+    po[1, 2] = 3.0
+    out = torch.empty((3, 256), dtype=torch.float16, device="cuda")
+    pg.paged_gqa_merge_partials(po, pl, out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[[0, 2]] == 0) and np.all(o[1] == 3.0)
+
+
 def test_graph_replay_bitwise(pg):
     import torch
 
@@ -233,7 +329,7 @@ def test_graph_replay_bitwise(pg):
     q, pool, table, lens = pg.device_case(case)
     n, hq, _ = q.shape
     wsb = pg.paged_gqa_workspace_bytes(n, hq, 1, case.max_seq_len, 0)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
     eager = torch.empty_like(q)
     pg.paged_gqa_decode(q, pool, table, lens, case.max_seq_len, case.sm_scale, eager,
                         workspace=ws)
