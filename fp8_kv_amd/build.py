@@ -23,6 +23,8 @@ FLAGS = [
     # Keep MFMA accumulators in ordinary VGPRs: the online softmax rescales
     # them with vector ALU ops every tile.
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # Leading scalar kernel arguments arrive preloaded in SGPRs.
+    "-mllvm", "-amdgpu-kernarg-preload-count=9",
 ]
 
 

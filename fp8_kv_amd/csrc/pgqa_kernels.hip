@@ -53,6 +53,15 @@ typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the merge buffer
 
+// Tile buffers per wave (tiles in flight while one is computed: depth - 1).
+#ifndef PGQA_PIPELINE_DEPTH
+#define PGQA_PIPELINE_DEPTH 2
+#endif
+// Tiles by which page-table entries are loaded ahead of their K/V loads.
+#ifndef PGQA_PAGE_LOOKAHEAD
+#define PGQA_PAGE_LOOKAHEAD 1
+#endif
+
 // ------------------------------------------------------------ E4M3 decode
 // Two E4M3 codes (bytes 2*HI, 2*HI+1 of w) to two fp16 values.  Every E4M3
 // value is exactly a binary16 value, so with a unit scale this is exact.
@@ -124,6 +133,7 @@ struct Wave {
   const AttnParams& p;
   const int32_t* tab;
   int64_t head_off;  // g * head_stride (bytes)
+  int64_t fallback;  // row offset read by lanes whose token is not live
   int s0, s1, wave, r, qd;
   h8_t qop[8];
   // running state
@@ -135,20 +145,32 @@ struct Wave {
     return s0 + (wave + NW * k) * kTile;
   }
 
-  // Page id (table entry) for this lane's K token of tile k; slot returned.
+  // Page-table entry (and slot) for this lane's K token of tile k.  The token
+  // is clamped to [0, max_len) only, so the load does not wait for the
+  // sequence length; entries of tokens past the live length are read but
+  // never used (issue() masks those lanes).
   __device__ __forceinline__ int fetch_page(int k, int& slot) const {
-    int t = min(tile_start(k) + r, s1 - 1);
+    int t = max(0, min(tile_start(k) + r, p.max_len - 1));
     int idx = div_page(t, p.page_size, p.inv_page_size, slot);
     return tab[idx];
   }
 
-  // Issue the K and V loads of a tile whose lane-token page/slot are known.
-  __device__ __forceinline__ void issue(TileRegs<FP8>& R, int page, int slot) {
-    bool ok = (page >= 0) & (page < p.num_pages);
-    bad |= !ok;
-    page = ok ? page : 0;
-    int64_t off = static_cast<int64_t>(page) * p.page_stride +
-                  static_cast<int64_t>(slot) * p.token_stride + head_off;
+  // Byte offset of a lane's row given its page-table entry (page 0 stands
+  // in for an out-of-range entry, so the address is always inside the pool).
+  __device__ __forceinline__ int64_t row_offset(int page, int slot) const {
+    const bool ok = (page >= 0) & (page < p.num_pages);
+    return static_cast<int64_t>(ok ? page : 0) * p.page_stride +
+           static_cast<int64_t>(slot) * p.token_stride + head_off;
+  }
+
+  // Issue the K and V loads of tile k.  Lanes whose token is not live read
+  // the fallback row (the wave's first live row: cached, finite); an
+  // out-of-range page id of a live token marks the wave's result bad.
+  __device__ __forceinline__ void issue(TileRegs<FP8>& R, int page, int slot, int k) {
+    const bool live = tile_start(k) + r < s1;
+    const bool ok = (page >= 0) & (page < p.num_pages);
+    bad |= live & !ok;
+    const int64_t off = live ? row_offset(page, slot) : fallback;
     const uint8_t* krow = p.k_base + off;
 #pragma unroll
     for (int i = 0; i < Geo<FP8>::kK; ++i) R.k[i] = load16(krow + 16 * (qd + 4 * i));
@@ -255,8 +277,25 @@ struct Wave {
   }
 };
 
-template <bool FP8, int NW>
-__global__ __launch_bounds__(64 * NW) void attention_kernel(AttnParams p) {
+constexpr int gcd_const(int a, int b) { return b == 0 ? a : gcd_const(b, a % b); }
+
+// The leading scalar arguments are what the first page-table load depends on;
+// the library is built with kernel-argument preloading, so they arrive in
+// SGPRs at wave launch and that load does not wait for the parameter block
+// (which is fetched from memory in parallel).
+template <bool FP8, int NW, int PD, int PL>
+__global__ __launch_bounds__(64 * NW) void attention_kernel(
+    const int32_t* table, const int32_t* lens, int32_t max_pages, int32_t max_len, int32_t chunk,
+    int32_t splits, int32_t hkv, int32_t page_size, float inv_page_size, AttnParams p) {
+  p.table = table;
+  p.lens = lens;
+  p.max_pages = max_pages;
+  p.max_len = max_len;
+  p.chunk = chunk;
+  p.splits = splits;
+  p.hkv = hkv;
+  p.page_size = page_size;
+  p.inv_page_size = inv_page_size;
   constexpr int kNT = 64 * NW;
   extern __shared__ float smem[];
   const int lane = threadIdx.x & 63;
@@ -269,31 +308,28 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(AttnParams p) {
   const int b = bg / p.hkv;
   const int g = bg - b * p.hkv;
 
-  const int L = min(p.lens[b], p.max_len);
+  const int Lraw = p.lens[b];  // its load overlaps the page-table prefetch below
   const int s0 = split * p.chunk;
-  const int s1 = min(s0 + p.chunk, L);
-  if (p.partials && s0 >= L) {
-    // A split with no live token: its partial is empty (lse = -inf).
-    if (threadIdx.x < p.group) {
-      const int64_t oh = static_cast<int64_t>(b) * p.hq + g * p.group + threadIdx.x;
-      p.ws_lse[oh * p.splits + split] = -__builtin_huge_valf();
-    }
-    return;
-  }
 
   Wave<FP8, NW> W{p};
   W.tab = p.table + static_cast<int64_t>(b) * p.max_pages;
   W.head_off = static_cast<int64_t>(g) * p.head_stride;
   W.s0 = s0;
-  W.s1 = s1;
   W.wave = wave;
   W.r = lane & 15;
   W.qd = lane >> 4;
-  W.m_run = -__builtin_huge_valf();
-  W.l_run = 0.f;
-  W.bad = false;
+
+  // Software pipeline over a ring of PD tile buffers: while tile k is
+  // computed, the K/V loads of tiles k+1 .. k+PD-1 are in flight.  Page-table
+  // entries run PL tiles further ahead, and each iteration loads them before
+  // its K/V loads (loads complete in issue order, so waiting for a page id
+  // never drains K/V loads issued after it).  The first entries are loaded
+  // before the sequence length is known, so they share its memory latency.
+  constexpr int RP = PL + 1;                      // page-entry ring
+  constexpr int U = PD * RP / gcd_const(PD, RP);  // unroll: ring indices are constants
+  int pg[RP], ps[RP];  // page-table entry and slot-in-page, per ring position
 #pragma unroll
-  for (int j = 0; j < 16; ++j) W.acc[j] = f4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t <= PD - 2 + PL; ++t) pg[t % RP] = W.fetch_page(t, ps[t % RP]);
 
   // q^T operand: head r of the group (zero past the group), the head-dim
   // pieces in the same permuted order as the K operand.
@@ -310,42 +346,44 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(AttnParams p) {
     }
   }
 
+  const int L = min(Lraw, p.max_len);
+  const int s1 = min(s0 + p.chunk, L);
+  if (p.partials && s0 >= L) {
+    // A split with no live token: its partial is empty (lse = -inf).
+    if (threadIdx.x < p.group) {
+      const int64_t oh = static_cast<int64_t>(b) * p.hq + g * p.group + threadIdx.x;
+      p.ws_lse[oh * p.splits + split] = -__builtin_huge_valf();
+    }
+    return;
+  }
+  W.s1 = s1;
+  W.m_run = -__builtin_huge_valf();
+  W.l_run = 0.f;
+  W.bad = false;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) W.acc[j] = f4_t{0.f, 0.f, 0.f, 0.f};
+
   const int span = s1 - s0 - wave * kTile;
   const int ntiles = span > 0 ? (span + NW * kTile - 1) / (NW * kTile) : 0;
 
-  // Software pipeline: while tile k is computed, tile k+1's K/V loads and
-  // tile k+2's page-table entries are in flight.  The page-table load of tile
-  // k+2 is issued before the K/V loads of tile k+1, so waiting for it later
-  // (loads complete in issue order) never drains tile k+1's loads.  The
-  // steady-state loop is straight-line so the wait counters stay precise; the
-  // last one to three tiles are peeled off after it.
+  // The loop body is straight-line so the wait counts are exact; it runs to a
+  // multiple of U tiles.  Tiles past the wave's range load only the cached
+  // fallback row and are not computed.
   if (ntiles > 0) {
-    TileRegs<FP8> A, B;
-    int slotA, slotB;
-    int pageA = W.fetch_page(0, slotA);
-    int pageB = W.fetch_page(1, slotB);
-    W.issue(A, pageA, slotA);
-    int k = 0;
-    for (; k + 3 < ntiles; k += 2) {
-      pageA = W.fetch_page(k + 2, slotA);
-      W.issue(B, pageB, slotB);
-      W.process(A, k);
-      pageB = W.fetch_page(k + 3, slotB);
-      W.issue(A, pageA, slotA);
-      W.process(B, k + 1);
-    }
-    // ntiles - k is 1, 2 or 3; A holds tile k, pageB is tile k+1's.
-    const bool has1 = k + 1 < ntiles;
-    const bool has2 = k + 2 < ntiles;
-    if (has1) {
-      pageA = W.fetch_page(k + 2, slotA);
-      W.issue(B, pageB, slotB);
-    }
-    W.process(A, k);
-    if (has1) {
-      if (has2) W.issue(A, pageA, slotA);
-      W.process(B, k + 1);
-      if (has2) W.process(A, k + 2);
+    // Lane 0's token of tile 0 is live (ntiles > 0): its row is the fallback.
+    W.fallback = __shfl(W.row_offset(pg[0], ps[0]), 0);
+    TileRegs<FP8> R[PD];
+#pragma unroll
+    for (int t = 0; t + 1 < PD; ++t) W.issue(R[t], pg[t % RP], ps[t % RP], t);
+    for (int k = 0; k < ntiles; k += U) {
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int tf = j + PD - 1 + PL;  // tile whose page entry is loaded now
+        const int ti = j + PD - 1;       // tile whose K/V loads are issued now
+        pg[tf % RP] = W.fetch_page(k + tf, ps[tf % RP]);
+        W.issue(R[ti % PD], pg[ti % RP], ps[ti % RP], k + ti);
+        if (k + j < ntiles) W.process(R[j % PD], k + j);
+      }
     }
   }
 
@@ -360,10 +398,15 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(AttnParams p) {
   const bool wave_bad = __ballot(W.bad) != 0;
   if (W.r < group) {
     float* row = so + (wave * group + W.r) * kLdsRow;
+    // acc[j][i] for j = 4jj .. 4jj+3 hold four consecutive head dims.
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) row[W.out_dim(j, i)] = W.acc[j][i];
+      for (int jj = 0; jj < 4; ++jj) {
+        float4 v = make_float4(W.acc[4 * jj][i], W.acc[4 * jj + 1][i], W.acc[4 * jj + 2][i],
+                               W.acc[4 * jj + 3][i]);
+        *reinterpret_cast<float4*>(row + W.out_dim(4 * jj, i)) = v;
+      }
     }
     if (W.qd == 0) {
       sm[wave * 16 + W.r] = W.m_run;
@@ -376,35 +419,44 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(AttnParams p) {
   bool any_bad = false;
 #pragma unroll
   for (int w = 0; w < NW; ++w) any_bad |= sflags[w] != 0;
-  for (int idx = threadIdx.x; idx < group * kHeadDim; idx += kNT) {
-    const int h = idx >> 8;
-    const int d = idx & (kHeadDim - 1);
+  // One item = (head h, four consecutive dims).
+  for (int item = threadIdx.x; item < group * (kHeadDim / 4); item += kNT) {
+    const int h = item / (kHeadDim / 4);
+    const int d = 4 * (item % (kHeadDim / 4));
     float M = -__builtin_huge_valf();
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w * 16 + h]);
-    float num = 0.f, den = 0.f;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    float den = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float mw = sm[w * 16 + h];
       if (mw != -__builtin_huge_valf()) {
         const float e = __builtin_amdgcn_exp2f(mw - M);
-        num += e * so[(w * group + h) * kLdsRow + d];
+        const float4 o = *reinterpret_cast<const float4*>(so + (w * group + h) * kLdsRow + d);
+        num.x += e * o.x;
+        num.y += e * o.y;
+        num.z += e * o.z;
+        num.w += e * o.w;
         den += e * sl[w * 16 + h];
       }
     }
+    // v_scale applied; an empty range (den = 0) gives zeros; a bad page NaNs.
+    const float scale = any_bad ? __builtin_nanf("") : (den > 0.f ? p.v_scale / den : 0.f);
+    num.x *= scale;
+    num.y *= scale;
+    num.z *= scale;
+    num.w *= scale;
     const int64_t oh = static_cast<int64_t>(b) * p.hq + g * group + h;
     if (!p.partials) {
-      float o = den > 0.f ? (num / den) * p.v_scale : 0.f;
-      if (any_bad) o = __builtin_nanf("");
-      p.out[oh * kHeadDim + d] = f16_bits(o);
+      u2_t packed;
+      packed[0] = f16_bits(num.x) | (static_cast<uint32_t>(f16_bits(num.y)) << 16);
+      packed[1] = f16_bits(num.z) | (static_cast<uint32_t>(f16_bits(num.w)) << 16);
+      *reinterpret_cast<u2_t*>(p.out + oh * kHeadDim + d) = packed;
     } else {
-      // With partials the split has a live token (or the sequence is empty
-      // and den = 0, lse = -inf).
-      float o = den > 0.f ? (num / den) * p.v_scale : 0.f;
-      if (any_bad) o = __builtin_nanf("");
-      p.ws_o[(oh * p.splits + split) * kHeadDim + d] = o;
-      if (d == 0) p.ws_lse[oh * p.splits + split] = den > 0.f ? M + __log2f(den)
-                                                             : -__builtin_huge_valf();
+      *reinterpret_cast<float4*>(p.ws_o + (oh * p.splits + split) * kHeadDim + d) = num;
+      if (d == 0)
+        p.ws_lse[oh * p.splits + split] = den > 0.f ? M + __log2f(den) : -__builtin_huge_valf();
     }
   }
 }
@@ -414,7 +466,11 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(AttnParams p) {
 // a split with lse = -inf (no live token) has weight 0 and its stored output
 // is not used.  The lse values and the partial outputs of a chunk of 32
 // splits are loaded together, so a chunk costs about one memory round trip.
-__global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
+__global__ __launch_bounds__(64) void merge_kernel(const float* lse_base, const float* o_base,
+                                                   int32_t splits, MergeParams p) {
+  p.lse = lse_base;  // leading arguments: preloaded into SGPRs
+  p.o = o_base;
+  p.splits = splits;
   constexpr int kChunk = 32;
   const int64_t row = blockIdx.x;
   const int lane = threadIdx.x;
@@ -474,18 +530,22 @@ __global__ void e4m3_table_kernel(float* out) {
 
 template <bool FP8, int NW>
 hipError_t launch(const AttnParams& p, hipStream_t stream) {
+  constexpr int PD = PGQA_PIPELINE_DEPTH;
+  constexpr int PL = PGQA_PAGE_LOOKAHEAD;
   const size_t lds = attention_lds_bytes(p.group, NW);
   if (lds > 65536) {
     // Merge buffers beyond the default 64 KiB dynamic LDS limit need the
     // limit raised (once per process and kernel).
     static const hipError_t raised = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(attention_kernel<FP8, NW>),
+        reinterpret_cast<const void*>(attention_kernel<FP8, NW, PD, PL>),
         hipFuncAttributeMaxDynamicSharedMemorySize,
         static_cast<int>(attention_lds_bytes(kMaxGroup, NW)));
     if (raised != hipSuccess) return raised;
   }
   const dim3 grid(static_cast<unsigned>(p.splits) * p.n * p.hkv);
-  hipLaunchKernelGGL((attention_kernel<FP8, NW>), grid, dim3(64 * NW), lds, stream, p);
+  hipLaunchKernelGGL((attention_kernel<FP8, NW, PD, PL>), grid, dim3(64 * NW), lds, stream,
+                     p.table, p.lens, p.max_pages, p.max_len, p.chunk, p.splits, p.hkv,
+                     p.page_size, p.inv_page_size, p);
   return hipGetLastError();
 }
 
@@ -505,7 +565,8 @@ hipError_t launch_attention(const AttnParams& p, bool fp8, hipStream_t stream) {
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(p.rows)), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(p.rows)), dim3(64), 0, stream, p.lse,
+                     p.o, p.splits, p);
   return hipGetLastError();
 }
 
