@@ -54,6 +54,7 @@ def measured_traffic(src_hash: str):
     return t.get("hbm_bytes_per_launch")
 
 
+
 def cpu_baseline(case, budget_s: float) -> dict:
     """The fp64 oracle, as it is, on the host cores: repeat whole calls on
     the same workload until about `budget_s` seconds have passed."""

@@ -26,7 +26,7 @@ using pgqa::kTile;
 #define PGQA_WAVES_PER_WG 4
 #endif
 #ifndef PGQA_WAVES_PER_CU
-#define PGQA_WAVES_PER_CU 8
+#define PGQA_WAVES_PER_CU 4
 #endif
 constexpr int kWaves = PGQA_WAVES_PER_WG;
 // Upper bound on splits (the merge reads every partial of a head).
