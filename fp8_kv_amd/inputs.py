@@ -184,16 +184,16 @@ def decode_case(*, batch: int, lens, page_size: int, kv_dtype: int,
 def sparse_prefill_case(*, rows: int, selected_blocks: int, tail: int, pool_blocks: int,
                         layout: str = "interleaved", seed: int = 0, num_q_heads: int = 6,
                         num_kv_heads: int = 1, head_dim: int = 256,
-                        kv_dtype: int = KV_FP16, scales="unit") -> PagedCase:
-    """Sparse prefill through virtual page-4 tables.
+                        kv_dtype: int = KV_FP16, scales="unit", page_size: int = 4) -> PagedCase:
+    """Sparse prefill through virtual page tables (page-4 by default).
 
     Row r owns block c_r = pool_blocks - rows + r (its causal block).  It
     selects `selected_blocks` distinct blocks uniformly from [0, c_r), sorted
     increasingly (locality order), then the partial page: the first `tail`
     tokens of block c_r (tail = 0 means no partial page).  Row length is
-    4*selected_blocks + tail.
+    page_size*selected_blocks + tail.
     """
-    P = 4
+    P = page_size
     assert 0 <= tail < P and pool_blocks - rows >= selected_blocks
     ss = np.random.SeedSequence(seed).spawn(6)
     rq, rk, rv, rt, rs, _ = (np.random.default_rng(s) for s in ss)
@@ -237,7 +237,37 @@ WORKLOADS = {
     "prefill_sparse_4096x2051_p4": dict(kind="prefill", rows=4096, selected_blocks=512,
                                          tail=3, pool_blocks=65536, layout="interleaved",
                                          seed=0),
+    # The page-16 selected-context sweep at 4096 rows (64, 512, 2048 tokens).
+    "prefill_sparse_4096x64_p16": dict(kind="prefill", rows=4096, selected_blocks=4, tail=0,
+                                        pool_blocks=16384, page_size=16,
+                                        layout="interleaved", seed=0),
+    "prefill_sparse_4096x512_p16": dict(kind="prefill", rows=4096, selected_blocks=32, tail=0,
+                                         pool_blocks=16384, page_size=16,
+                                         layout="interleaved", seed=0),
+    "prefill_sparse_4096x2048_p16": dict(kind="prefill", rows=4096, selected_blocks=128,
+                                          tail=0, pool_blocks=16384, page_size=16,
+                                          layout="interleaved", seed=0),
 }
+
+
+def hybrid_784_16_case(*, batch: int, blocks_per_seq: int, lens, kv_dtype: int = KV_FP16,
+                       seed: int = 0, layout: str = "contiguous") -> PagedCase:
+    """The hybrid 784/16 geometry: the allocator hands out blocks of 784
+    tokens, which the kernel reads as 49 pages of 16 tokens; a sequence's
+    page-16 table lists, for each of its allocator blocks (taken in a random,
+    nonmonotonic order), that block's 49 kernel pages in order (physical page
+    ids in kernel-page units)."""
+    sub = 784 // 16
+    n_blocks = batch * blocks_per_seq
+    case = decode_case(batch=batch, lens=lens, page_size=16, kv_dtype=kv_dtype, seed=seed,
+                       layout=layout, num_pages=n_blocks * sub, table="identity",
+                       max_seq_len=blocks_per_seq * 784)
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(7)[6])
+    blocks = rng.permutation(n_blocks).reshape(batch, blocks_per_seq)
+    tab = (blocks[:, :, None] * sub + np.arange(sub)[None, None, :]).reshape(batch, -1)
+    case.table = np.ascontiguousarray(tab, dtype=np.int32)
+    case.meta = dict(allocator_block=784, kernel_page=16)
+    return case
 
 
 def workload_case(name: str, **overrides) -> PagedCase:

@@ -127,6 +127,49 @@ def test_split_counts_long_context(pg, splits):
     _check(pg, case, f"splits {splits}", num_splits=splits)
 
 
+@pytest.mark.parametrize("batch", [2, 16])
+@pytest.mark.parametrize("page_size", [64, 128, 256])
+def test_decode_batch_page_matrix(pg, batch, page_size):
+    """B2/B16 at pages 64/128/256 with E4M3 KV, as in the decode operator checks."""
+    case = inputs.decode_case(batch=batch, lens=("uniform", 1, 4096), page_size=page_size,
+                              kv_dtype=E4M3, seed=80 + page_size + batch, scales="uniform",
+                              max_seq_len=4096)
+    _check(pg, case, f"B{batch} P{page_size}")
+
+
+@pytest.mark.parametrize("kv_dtype", [FP16, E4M3])
+def test_page_784(pg, kv_dtype):
+    case = inputs.decode_case(batch=3, lens=[2000, 784, 785], page_size=784, kv_dtype=kv_dtype,
+                              seed=90, scales="uniform")
+    for s in (1, 0):
+        _check(pg, case, f"P784 dtype{kv_dtype} splits{s}", num_splits=s)
+
+
+def test_hybrid_784_16_geometry(pg):
+    """784-token allocator blocks read as page-16 kernel pages, with a
+    nonmonotonic 128-entry page-16 table per sequence."""
+    case = inputs.hybrid_784_16_case(batch=4, blocks_per_seq=3, lens=[2048, 2048, 1500, 31],
+                                     seed=91)
+    assert case.table.shape[1] >= 128
+    assert not np.all(np.diff(case.table[0, :128]) == 1)
+    # Sequence 0's first 128 entries cover its 2048 tokens.
+    _check(pg, case, "hybrid 784/16")
+    # Same tokens through page-784 kernel pages give the same attention.
+    case784 = dataclasses.replace(
+        case, page_size=784, num_pages=case.num_pages // 49,
+        page_stride=case.page_stride * 49,
+        table=np.ascontiguousarray(case.table[:, ::49] // 49, dtype=np.int32))
+    # Same tokens in the same 16-token tiles: the results are bitwise equal.
+    for s in (1, 4):
+        assert np.array_equal(_run(pg, case, num_splits=s), _run(pg, case784, num_splits=s))
+
+
+def test_sparse_prefill_page16(pg):
+    case = inputs.sparse_prefill_case(rows=40, selected_blocks=32, tail=0, pool_blocks=300,
+                                      page_size=16, seed=92)
+    _check(pg, case, "prefill page 16", prefill=True)
+
+
 def test_sparse_prefill_tails(pg):
     for tail in (1, 2, 3, 0):
         case = inputs.sparse_prefill_case(rows=64, selected_blocks=40, tail=tail,
