@@ -278,3 +278,103 @@ def workload_case(name: str, **overrides) -> PagedCase:
         spec.setdefault("kv_dtype", KV_E4M3)
         return decode_case(**spec)
     return sparse_prefill_case(**spec)
+
+
+# ---------------------------------------------------------------- QSA top-k
+@dataclass
+class TopkCase:
+    """Block scores for QSA top-k selection ("[Kernel][SM70] Accelerate exact
+    Qwen3.8 decode", Implementation): fp32 scores [rows][row_stride], of which
+    row r's first n_valid[r] blocks are eligible; k blocks are kept per row."""
+    scores: np.ndarray          # float32 [rows][row_stride]
+    n_valid: np.ndarray         # int32 [rows]
+    n_blocks: int               # columns the selection may look at (<= row_stride)
+    k: int
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def rows(self) -> int:
+        return int(self.scores.shape[0])
+
+    def score_bytes(self) -> int:
+        """Bytes of scores a selection must read: the eligible prefixes."""
+        nv = np.clip(self.n_valid.astype(np.int64), 0, self.n_blocks)
+        return int(nv.sum()) * 4
+
+
+def topk_case(*, rows: int, n_blocks: int, k: int, seed: int, dist: str = "normal",
+              n_valid="full", row_stride: int | None = None) -> TopkCase:
+    """Seeded block scores.
+
+    dist: "normal" (N(0,1) fp32), "ties" (N(0,1) rounded to multiples of 1/4,
+    so many blocks share a score), "constant" (every score 0.5), "special"
+    (normal draws with +-inf, +-0 and NaNs of both signs mixed in), "ramp"
+    (score j = j, increasing with the block index).
+    n_valid: "full" (every row sees n_blocks), "causal" (row r sees
+    n_blocks - rows + r blocks, the last rows of a prefill chunk), "random"
+    (uniform in [0, n_blocks], with 0, 1 and n_blocks forced into the first
+    rows), an int, or an explicit per-row sequence.
+    Seeds: SeedSequence(seed).spawn(2) children draw the scores and the
+    lengths, in that order.
+    """
+    stride = n_blocks if row_stride is None else int(row_stride)
+    assert stride >= n_blocks
+    s_rng, l_rng = (np.random.default_rng(c) for c in np.random.SeedSequence(seed).spawn(2))
+    shape = (rows, stride)
+    if dist == "normal":
+        sc = s_rng.standard_normal(shape, dtype=np.float32)
+    elif dist == "ties":
+        sc = np.round(s_rng.standard_normal(shape, dtype=np.float32) * 4) / 4
+    elif dist == "constant":
+        sc = np.full(shape, 0.5, dtype=np.float32)
+    elif dist == "special":
+        sc = s_rng.standard_normal(shape, dtype=np.float32)
+        specials = np.array([np.inf, -np.inf, 0.0, -0.0, np.nan, -np.nan], dtype=np.float32)
+        specials_bits = specials.view(np.uint32).copy()
+        specials_bits[5] |= 0x80000000     # a negative NaN
+        specials = specials_bits.view(np.float32)
+        pick = s_rng.random(shape) < 0.05
+        sc[pick] = specials[s_rng.integers(0, len(specials), size=int(pick.sum()))]
+    elif dist == "ramp":
+        sc = np.broadcast_to(np.arange(stride, dtype=np.float32), shape).copy()
+    else:
+        raise ValueError(dist)
+    sc = np.ascontiguousarray(sc.astype(np.float32))
+    if isinstance(n_valid, str):
+        if n_valid == "full":
+            nv = np.full(rows, n_blocks, dtype=np.int32)
+        elif n_valid == "causal":
+            nv = (n_blocks - rows + np.arange(rows)).astype(np.int32)
+            assert nv.min() >= 0
+        elif n_valid == "random":
+            nv = l_rng.integers(0, n_blocks + 1, size=rows).astype(np.int32)
+            nv[:3] = [0, 1, n_blocks][:min(3, rows)]
+        else:
+            raise ValueError(n_valid)
+    elif np.isscalar(n_valid):
+        nv = np.full(rows, int(n_valid), dtype=np.int32)
+    else:
+        nv = np.asarray(n_valid, dtype=np.int32)
+        assert nv.shape == (rows,)
+    return TopkCase(scores=sc, n_valid=np.ascontiguousarray(nv), n_blocks=n_blocks, k=k,
+                    meta=dict(seed=seed, dist=dist))
+
+
+# The QSA selection keeps 512 four-token blocks per query (the 2051-token
+# selection layout of "[Kernel][SM70] Accelerate Qwen3.8 QSA paged prefill",
+# Changes).  Decode: one sequence at 8,192 input + 512 output tokens (the speed
+# gate of "[Kernel][SM70] Accelerate exact Qwen3.8 decode", Scope and
+# contract) has 2,176 blocks.  Prefill: the 4096 rows of the sparse-prefill
+# workload, row r with 61,440 + r complete blocks behind it (262,144-token
+# maximum length, page-4 blocks).
+TOPK_WORKLOADS = {
+    "qsa_topk_decode_1x2176_k512": dict(rows=1, n_blocks=2176, k=512, seed=71),
+    "qsa_topk_prefill_4096x65536_k512": dict(rows=4096, n_blocks=65536, k=512, seed=72,
+                                             n_valid="causal"),
+}
+
+
+def topk_workload_case(name: str, **overrides) -> TopkCase:
+    kw = dict(TOPK_WORKLOADS[name])
+    kw.update(overrides)
+    return topk_case(**kw)

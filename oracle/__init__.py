@@ -16,4 +16,5 @@ from .oracle import (  # noqa: F401
     load,
     num_threads,
     paged_gqa,
+    topk_select,
 )

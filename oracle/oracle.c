@@ -1,5 +1,6 @@
 /*
- * oracle.c -- plain fp64 CPU oracle for paged grouped-query attention.
+ * oracle.c -- plain CPU oracle for paged grouped-query attention (fp64) and
+ * for QSA top-k block selection (exact integer/ordering work).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
  * load this file; only the tests, the smoke check and the benchmark's CPU
@@ -24,6 +25,13 @@
  *      o_h = sum_t w_t V_t / sum_t w_t,  and o_h = 0 for an empty sequence.
  * No blocking, fusion or reordering beyond that.  Parallelism: one OpenMP
  * task per (sequence, kv head) pair; each pair is computed serially.
+ *
+ * QSA top-k selection ("[Kernel][SM70] Accelerate exact Qwen3.8 decode",
+ * Implementation) is exact as well, so the oracle is its definition: a full
+ * sort of each row by (score descending, index ascending), the first k kept,
+ * reported in increasing index order.  Pinned by numpy's stable argsort,
+ * brute-force rank counting, the IEEE totalOrder spot list
+ * (tests/golden/fp32_total_order.txt), closed forms and invariants.
  *
  * Every function here is pinned by the CPU test suite (closed forms,
  * invariants, and library routines: torch's float8_e4m3fn cast, numpy's
@@ -207,6 +215,76 @@ int oracle_paged_gqa(const uint16_t* q, int32_t n_seq, int32_t Hq, int32_t Hkv,
       }
     }
     free(Kd); free(Vd); free(z); free(qd);
+  }
+  return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Top-k block selection ("[Kernel][SM70] Accelerate exact Qwen3.8 decode",
+ * Implementation: QSA selection by score with increasing-index tie order at
+ * the pivot).  Definition: order the row's eligible blocks j < n_valid by
+ * (score descending, index ascending), keep the first min(k, n_valid), and
+ * report the kept indices in increasing order.  Scores are ranked by their
+ * IEEE-754 bit patterns mapped to an order-preserving unsigned key (so -0.0
+ * ranks just below +0.0; two scores tie only when their bits are equal).
+ */
+static uint32_t score_key(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+typedef struct {
+  uint32_t key;
+  int32_t idx;
+} keyed_t;
+
+static int cmp_rank(const void* a, const void* b) {
+  const keyed_t* x = (const keyed_t*)a;
+  const keyed_t* y = (const keyed_t*)b;
+  if (x->key != y->key) return x->key > y->key ? -1 : 1; /* larger score first */
+  return x->idx < y->idx ? -1 : (x->idx > y->idx ? 1 : 0); /* then lower index */
+}
+
+static int cmp_int(const void* a, const void* b) {
+  int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return x < y ? -1 : (x > y ? 1 : 0);
+}
+
+/* scores: [rows][row_stride] fp32; n_valid: [rows] eligible prefix lengths
+ * (NULL = all n_blocks); out_idx: [rows][k] (kept indices ascending, then -1);
+ * out_count: [rows] number kept. */
+int oracle_topk_select(const float* scores, int64_t row_stride, const int32_t* n_valid,
+                       int32_t rows, int32_t n_blocks, int32_t k, int32_t* out_idx,
+                       int32_t* out_count) {
+  if (!scores || !out_idx || !out_count || rows < 0 || n_blocks < 0 || k < 0 ||
+      row_stride < n_blocks)
+    return ORACLE_ERR_ARG;
+  int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t r = 0; r < rows; ++r) {
+    int32_t m = n_valid ? n_valid[r] : n_blocks;
+    if (m < 0) m = 0;
+    if (m > n_blocks) m = n_blocks;
+    keyed_t* items = (keyed_t*)malloc(sizeof(keyed_t) * (size_t)(m > 0 ? m : 1));
+    if (!items) {
+#pragma omp atomic write
+      failed = 1;
+      continue;
+    }
+    const float* row = scores + (int64_t)r * row_stride;
+    for (int32_t j = 0; j < m; ++j) {
+      items[j].key = score_key(row[j]);
+      items[j].idx = j;
+    }
+    qsort(items, (size_t)m, sizeof(keyed_t), cmp_rank);
+    int32_t t = m < k ? m : k;
+    int32_t* o = out_idx + (int64_t)r * k;
+    for (int32_t i = 0; i < t; ++i) o[i] = items[i].idx;
+    qsort(o, (size_t)t, sizeof(int32_t), cmp_int);
+    for (int32_t i = t; i < k; ++i) o[i] = -1;
+    out_count[r] = t;
+    free(items);
   }
   return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
 }

@@ -70,6 +70,10 @@ def load(path: str = _LIB) -> ctypes.CDLL:
         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_double,
         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
     ]
+    lib.oracle_topk_select.restype = ctypes.c_int
+    lib.oracle_topk_select.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_void_p]
     _lib_cache[path] = lib
     return lib
 
@@ -140,3 +144,23 @@ def paged_gqa(*, q: np.ndarray, k_store: np.ndarray, v_store: np.ndarray,
     if rc != 0:
         raise OracleError(rc)
     return out
+
+
+def topk_select(scores: np.ndarray, k: int, n_valid=None, n_blocks: int | None = None,
+                lib_path: str = _LIB):
+    """Top-k block selection per row (see oracle.c).  scores: float32
+    [rows][row_stride], of which the first n_blocks columns (default: all) may
+    be selected.  Returns (idx int32 [rows][k] ascending then -1,
+    count int32 [rows])."""
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    rows, stride = scores.shape
+    nb = stride if n_blocks is None else int(n_blocks)
+    nv = None if n_valid is None else np.ascontiguousarray(n_valid, dtype=np.int32)
+    idx = np.empty((rows, k), dtype=np.int32)
+    cnt = np.empty(rows, dtype=np.int32)
+    rc = load(lib_path).oracle_topk_select(scores.ctypes.data, stride,
+                                           None if nv is None else nv.ctypes.data,
+                                           rows, nb, k, idx.ctypes.data, cnt.ctypes.data)
+    if rc != 0:
+        raise OracleError(rc)
+    return idx, cnt

@@ -319,5 +319,153 @@ def pin_errors(lib: str) -> None:
         assert e.code == oracle.ORACLE_ERR_TABLE
 
 
+# ------------------------------------------------------ QSA top-k selection
+def _check_topk_layout(idx, cnt, k, nv):
+    """Shape facts every selection result has: count = min(k, nv), the kept
+    indices strictly increasing inside [0, nv), then -1 padding."""
+    for r in range(idx.shape[0]):
+        want = min(k, max(0, int(nv[r])))
+        assert cnt[r] == want, (r, cnt[r], want)
+        kept = idx[r, :want]
+        assert np.all(np.diff(kept) > 0), r
+        assert want == 0 or (kept[0] >= 0 and kept[-1] < nv[r]), r
+        assert np.all(idx[r, want:] == -1), r
+
+
+def pin_topk_vs_stable_sort(lib: str) -> None:
+    """Against numpy's stable argsort of the negated scores: the first k of
+    that order are the top-k with ties broken by increasing index.  -0.0 is
+    folded into +0.0 first, since float comparison ties them."""
+    for dist, k in (("normal", 7), ("ties", 16), ("ties", 1), ("constant", 5), ("normal", 300)):
+        case = inputs.topk_case(rows=24, n_blocks=257, k=k, seed=31 + k, dist=dist,
+                                n_valid="random")
+        sc = case.scores + np.float32(0.0)
+        idx, cnt = oracle.topk_select(sc, k, case.n_valid, lib_path=lib)
+        _check_topk_layout(idx, cnt, k, case.n_valid)
+        for r in range(case.rows):
+            nv = int(case.n_valid[r])
+            order = np.argsort(-sc[r, :nv].astype(np.float64), kind="stable")
+            want = np.sort(order[:k])
+            assert np.array_equal(idx[r, :len(want)], want), (dist, k, r)
+
+
+def pin_topk_brute_force(lib: str) -> None:
+    """Every length-5 score vector over {-inf, -1, 0, 1, +inf} and every k:
+    block j is kept iff fewer than k blocks outrank it, where i outranks j when
+    s_i > s_j, or s_i == s_j and i < j (Python float comparison)."""
+    import itertools
+    vals = [-math.inf, -1.0, 0.0, 1.0, math.inf]
+    rows = np.array(list(itertools.product(vals, repeat=5)), dtype=np.float32)
+    n = rows.shape[1]
+    for k in range(0, n + 2):
+        idx, cnt = oracle.topk_select(rows, k, lib_path=lib)
+        for r, sv in enumerate(rows.tolist()):
+            kept = [j for j in range(n)
+                    if sum(1 for i in range(n)
+                           if sv[i] > sv[j] or (sv[i] == sv[j] and i < j)) < k]
+            assert cnt[r] == len(kept) and idx[r, :len(kept)].tolist() == kept, (k, sv)
+            assert np.all(idx[r, len(kept):] == -1)
+
+
+def pin_topk_total_order(lib: str) -> None:
+    """Special values (tests/golden/fp32_total_order.txt, IEEE 754 totalOrder)
+    shuffled into a row: the k kept blocks are always the k highest in the
+    golden order."""
+    bits = []
+    with open(os.path.join(GOLDEN, "fp32_total_order.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                bits.append(int(line.split()[0], 16))
+    assert len(bits) >= 19
+    rng = np.random.default_rng(5)
+    for trial in range(4):
+        perm = rng.permutation(len(bits))
+        row = np.array([bits[p] for p in perm], dtype=np.uint32).view(np.float32)[None, :]
+        rank_of_pos = perm                      # position j holds golden rank perm[j]
+        for k in range(len(bits) + 1):
+            idx, cnt = oracle.topk_select(row, k, lib_path=lib)
+            want = sorted(j for j in range(len(bits)) if rank_of_pos[j] >= len(bits) - k)
+            assert idx[0, :cnt[0]].tolist() == want, (trial, k)
+
+
+def pin_topk_closed_forms(lib: str) -> None:
+    n = 100
+    ramp = np.arange(n, dtype=np.float32)[None, :]
+    idx, cnt = oracle.topk_select(ramp, 10, lib_path=lib)
+    assert idx[0].tolist() == list(range(90, 100))            # increasing: last k
+    idx, _ = oracle.topk_select(ramp[:, ::-1].copy(), 10, lib_path=lib)
+    assert idx[0].tolist() == list(range(10))                  # decreasing: first k
+    idx, _ = oracle.topk_select(np.full((1, n), 3.0, np.float32), 10, lib_path=lib)
+    assert idx[0].tolist() == list(range(10))                  # all tied: lowest indices
+    neg = -np.arange(1, n + 1, dtype=np.float32)[None, :]      # -1, -2, ...: first k
+    idx, _ = oracle.topk_select(neg, 4, lib_path=lib)
+    assert idx[0].tolist() == [0, 1, 2, 3]
+    # One block above a sea of ties: it plus the lowest tied indices.
+    row = np.zeros((1, n), np.float32)
+    row[0, 77] = 1.0
+    idx, _ = oracle.topk_select(row, 3, lib_path=lib)
+    assert idx[0].tolist() == [0, 1, 77]
+    # Fewer eligible blocks than k: all of them, then padding.
+    idx, cnt = oracle.topk_select(ramp, 10, n_valid=[6], lib_path=lib)
+    assert cnt[0] == 6 and idx[0].tolist() == list(range(6)) + [-1] * 4
+    # k = 0, an empty row, a negative length, a length past n_blocks.
+    idx, cnt = oracle.topk_select(ramp, 0, lib_path=lib)
+    assert idx.shape == (1, 0) and cnt[0] == 0
+    idx, cnt = oracle.topk_select(np.repeat(ramp, 3, 0), 2, n_valid=[0, -5, 10**6], lib_path=lib)
+    assert cnt.tolist() == [0, 0, 2] and idx[:2].tolist() == [[-1, -1], [-1, -1]]
+    assert idx[2].tolist() == [98, 99]
+    # Columns past n_blocks are never looked at.
+    wide = np.concatenate([ramp, np.full((1, 28), np.inf, np.float32)], axis=1)
+    idx, _ = oracle.topk_select(wide, 3, n_blocks=n, lib_path=lib)
+    assert idx[0].tolist() == [97, 98, 99]
+
+
+def pin_topk_invariants(lib: str) -> None:
+    case = inputs.topk_case(rows=16, n_blocks=1000, k=64, seed=44, dist="ties",
+                            n_valid="random")
+    sc = case.scores + np.float32(0.0)
+    idx, cnt = oracle.topk_select(sc, case.k, case.n_valid, lib_path=lib)
+    _check_topk_layout(idx, cnt, case.k, case.n_valid)
+    for r in range(case.rows):
+        nv = int(case.n_valid[r])
+        kept = idx[r, :cnt[r]]
+        mask = np.zeros(nv, bool)
+        mask[kept] = True
+        if mask.all() or not mask.any():
+            continue
+        lo, hi = sc[r, :nv][mask].min(), sc[r, :nv][~mask].max()
+        assert lo >= hi, r                              # kept outrank dropped
+        if lo == hi:                                    # ties at the pivot: low indices first
+            tied = np.flatnonzero(sc[r, :nv] == lo)
+            assert mask[tied].tolist() == sorted(mask[tied].tolist(), reverse=True), r
+    # Rows are independent: one row at a time gives the same answer.
+    for r in (0, 5, 11):
+        i1, c1 = oracle.topk_select(sc[r:r + 1], case.k, case.n_valid[r:r + 1], lib_path=lib)
+        assert np.array_equal(i1[0], idx[r]) and c1[0] == cnt[r]
+    # Moving distinct scores around moves the kept set with them.
+    row = inputs.topk_case(rows=1, n_blocks=500, k=40, seed=45).scores
+    assert len(np.unique(row)) == row.size
+    perm = np.random.default_rng(9).permutation(row.shape[1])
+    i0, _ = oracle.topk_select(row, 40, lib_path=lib)
+    i1, _ = oracle.topk_select(row[:, perm], 40, lib_path=lib)
+    inv = np.argsort(perm)
+    assert np.array_equal(np.sort(inv[i0[0]]), i1[0])
+
+
+def pin_topk_errors(lib: str) -> None:
+    """Negative sizes and a row stride shorter than the row are rejected."""
+    c = oracle.load(lib)
+    sc = np.zeros((2, 4), np.float32)
+    out = np.zeros(16, np.int32)
+    cnt = np.zeros(2, np.int32)
+    args = lambda stride, rows, nb, k: (sc.ctypes.data, stride, None, rows, nb, k,  # noqa: E731
+                                        out.ctypes.data, cnt.ctypes.data)
+    assert c.oracle_topk_select(*args(4, 2, 4, 2)) == 0
+    for bad in (args(4, 2, 4, -1), args(4, -1, 4, 2), args(3, 2, 4, 2), args(4, 2, -2, 2)):
+        assert c.oracle_topk_select(*bad) == oracle.ORACLE_ERR_ARG, bad[1:6]
+
+
 ALL_PINS = [pin_e4m3_vs_torch, pin_e4m3_golden, pin_f16_vs_numpy, pin_sdpa,
-            pin_sparse_vs_masked_sdpa, pin_closed_forms, pin_invariants, pin_errors]
+            pin_sparse_vs_masked_sdpa, pin_closed_forms, pin_invariants, pin_errors,
+            pin_topk_vs_stable_sort, pin_topk_brute_force, pin_topk_total_order,
+            pin_topk_closed_forms, pin_topk_invariants, pin_topk_errors]

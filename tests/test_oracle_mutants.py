@@ -40,6 +40,19 @@ MUTANTS = {
     "last_token_dropped": ("for (int32_t t = 0; t < L; ++t) {\n      int64_t page",
                            "for (int32_t t = 0; t < L - 1; ++t) {\n      int64_t page"),
     "empty_not_inert": ("if (L <= 0) {\n      memset", "if (L < 0) {\n      memset"),
+    "topk_ascending": ("if (x->key != y->key) return x->key > y->key ? -1 : 1;",
+                       "if (x->key != y->key) return x->key < y->key ? -1 : 1;"),
+    "topk_tie_order": ("return x->idx < y->idx ? -1 : (x->idx > y->idx ? 1 : 0);",
+                       "return x->idx > y->idx ? -1 : (x->idx < y->idx ? 1 : 0);"),
+    "topk_negative_key": ("return (u & 0x80000000u) ? ~u : (u | 0x80000000u);",
+                          "return (u & 0x80000000u) ? u : (u | 0x80000000u);"),
+    "topk_sign_flip_key": ("return (u & 0x80000000u) ? ~u : (u | 0x80000000u);",
+                           "return u ^ 0x80000000u;"),
+    "topk_n_valid_ignored": ("int32_t m = n_valid ? n_valid[r] : n_blocks;",
+                             "int32_t m = n_blocks;"),
+    "topk_one_short": ("int32_t t = m < k ? m : k;", "int32_t t = m < k ? m : k - 1;"),
+    "topk_rank_order_out": ("qsort(o, (size_t)t, sizeof(int32_t), cmp_int);", ";"),
+    "topk_no_clamp": ("if (m > n_blocks) m = n_blocks;", ";"),
 }
 
 
