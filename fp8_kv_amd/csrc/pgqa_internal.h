@@ -51,9 +51,26 @@ struct MergeParams {
   uint16_t* out;           // fp16 bits [rows][256]
 };
 
+// QSA top-k block selection (qsa_topk.hip): one workgroup per row.
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkMaxBlocks = 65536;   // blocks per row held in registers
+
+struct TopkParams {
+  const float* scores;     // [rows][row_stride]
+  int64_t row_stride;      // elements
+  const int32_t* n_valid;  // [rows] or nullptr (= n_blocks)
+  int32_t rows;
+  int32_t n_blocks;        // <= kTopkMaxBlocks
+  int32_t k;
+  int32_t* out_idx;        // [rows][k]
+  int32_t* out_count;      // [rows] or nullptr
+};
+
 hipError_t launch_attention(const AttnParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_e4m3_table(float* out256, hipStream_t stream);
 size_t attention_lds_bytes(int group, int waves);
+// vec: scores 16-byte aligned, row_stride and n_blocks multiples of 4.
+hipError_t launch_topk(const TopkParams& p, bool vec, hipStream_t stream);
 
 }  // namespace pgqa

@@ -30,7 +30,8 @@ SIZE_MAX = ctypes.c_size_t(-1).value
 # Every symbol include/pgqa.h declares.
 EXPORTS = ("paged_gqa_workspace_bytes", "paged_gqa_num_splits", "paged_gqa_decode",
            "paged_gqa_prefill_sparse", "paged_gqa_decode_partial", "paged_gqa_merge_partials",
-           "e4m3_decode_table", "pgqa_error_string")
+           "e4m3_decode_table", "qsa_topk_select", "pgqa_error_string")
+QSA_MAX_BLOCKS = 65536
 
 
 class PgqaError(RuntimeError):
@@ -81,6 +82,8 @@ def _lib(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_gqa_merge_partials.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.e4m3_decode_table.restype = ctypes.c_int
     lib.e4m3_decode_table.argtypes = [vp, vp]
+    lib.qsa_topk_select.restype = ctypes.c_int
+    lib.qsa_topk_select.argtypes = [vp, ctypes.c_int64, vp, i32, i32, i32, vp, vp, vp]
     lib.pgqa_error_string.restype = ctypes.c_char_p
     lib.pgqa_error_string.argtypes = [ctypes.c_int]
     _LIB = lib
@@ -206,6 +209,32 @@ def paged_gqa_merge_partials(part_o, part_lse, out, stream=None) -> None:
 def e4m3_decode_table(out, stream=None) -> None:
     """out: float32 [256] device tensor."""
     _check(_lib().e4m3_decode_table(_ptr(out), _stream_handle(stream)), "e4m3_decode_table")
+
+
+def qsa_topk_select(scores, k: int, n_valid=None, n_blocks: int | None = None, out_idx=None,
+                    out_count=None, stream=None):
+    """QSA top-k block selection per row.
+
+    scores: fp32 device tensor [rows][n] (row stride taken from the tensor);
+    the first n_blocks columns (default n) may be selected, row r only its
+    first n_valid[r].  Returns (out_idx int32 [rows][k], out_count int32
+    [rows]), allocating them when not given."""
+    import torch
+
+    if scores.dim() != 2 or scores.dtype != torch.float32 or scores.stride(1) != 1:
+        raise ValueError("scores must be a float32 [rows][n] tensor with unit column stride")
+    rows = scores.shape[0]
+    nb = scores.shape[1] if n_blocks is None else int(n_blocks)
+    if out_idx is None:
+        out_idx = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    if out_count is None:
+        out_count = torch.empty(rows, dtype=torch.int32, device=scores.device)
+    stride = scores.stride(0) if rows > 1 else max(scores.shape[1], nb)
+    rc = _lib().qsa_topk_select(_ptr(scores), int(stride), _ptr(n_valid), int(rows), int(nb),
+                                int(k), _ptr(out_idx) if k > 0 else None, _ptr(out_count),
+                                _stream_handle(stream))
+    _check(rc, "qsa_topk_select")
+    return out_idx, out_count
 
 
 # ------------------------------------------------------------ device inputs

@@ -199,6 +199,40 @@ int paged_gqa_merge_partials(const float* part_o, const float* part_lse, int32_t
  */
 int e4m3_decode_table(float* out256, void* stream);
 
+/*
+ * QSA top-k block selection (source: "[Kernel][SM70] Accelerate exact Qwen3.8
+ * decode", Implementation -- the QSA selection takes the top-k block scores
+ * with score radix passes and keeps ties at the pivot in increasing index
+ * order).  For each row r, the eligible blocks are j = 0 .. m_r - 1 with
+ * m_r = clamp(n_valid[r], 0, n_blocks) (n_valid NULL: m_r = n_blocks).  The
+ * kept set is the first min(k, m_r) blocks in the order (score descending,
+ * index ascending), where scores are ranked by IEEE 754 totalOrder of their
+ * fp32 bit patterns (-NaN < -inf < ... < -0 < +0 < ... < +inf < +NaN; two
+ * scores tie only when their bits are equal).
+ *
+ *   scores     fp32 [rows][row_stride] (device), row r at scores + r*row_stride;
+ *              only columns < n_blocks are read, and of row r only < m_r.
+ *              4-byte aligned; 16-byte alignment with row_stride and n_blocks
+ *              multiples of 4 takes the vector-load path.
+ *   row_stride elements, >= n_blocks.
+ *   n_valid    int32 [rows] (device) or NULL.
+ *   rows       >= 0 (0: nothing is launched).
+ *   n_blocks   0 .. PGQA_QSA_MAX_BLOCKS.
+ *   k          0 .. PGQA_QSA_MAX_BLOCKS.
+ *   out_idx    int32 [rows][k] (device): row r's kept block indices in
+ *              increasing order, then -1 in the remaining k - min(k, m_r)
+ *              entries.  May be NULL only when k == 0.
+ *   out_count  int32 [rows] (device) or NULL: min(k, m_r).
+ * Errors: PGQA_ERR_NULL (scores, or out_idx with k > 0, missing while
+ * rows > 0), PGQA_ERR_SHAPE (negative rows/k, n_blocks or k out of range),
+ * PGQA_ERR_LAYOUT (row_stride < n_blocks or misaligned pointers),
+ * PGQA_ERR_HIP (launch refused).
+ */
+#define PGQA_QSA_MAX_BLOCKS 65536 /* 262,144 tokens in 4-token blocks */
+int qsa_topk_select(const float* scores, int64_t row_stride, const int32_t* n_valid,
+                    int32_t rows, int32_t n_blocks, int32_t k, int32_t* out_idx,
+                    int32_t* out_count, void* stream);
+
 /* Static description of a return code. */
 const char* pgqa_error_string(int code);
 

@@ -29,13 +29,14 @@ class OracleError(RuntimeError):
 
 def build(out_path: str = _LIB, extra_flags: tuple[str, ...] = ()) -> str:
     """Compile oracle.c with gcc into a shared library (IEEE fp64, no contraction)."""
+    tmp = f"{out_path}.{os.getpid()}.tmp"   # concurrent builders never share a temp file
     cmd = [
         "gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
         "-ffp-contract=off", "-fno-fast-math", *extra_flags,
-        _SRC, "-o", out_path + ".tmp", "-lm",
+        _SRC, "-o", tmp, "-lm",
     ]
     subprocess.run(cmd, check=True)
-    os.replace(out_path + ".tmp", out_path)
+    os.replace(tmp, out_path)
     return out_path
 
 

@@ -161,3 +161,34 @@ def test_error_strings(lib):
     for code in range(-7, 1):
         assert lib.pgqa_error_string(code)
     assert lib.pgqa_error_string(-99) == b"unknown error code"
+
+
+def test_topk_validation(lib):
+    """qsa_topk_select: every rejected call returns before any HIP call."""
+    f = lib.qsa_topk_select
+    ok = dict(scores=FAKE, stride=64, nv=None, rows=2, nb=64, k=8, out=FAKE, cnt=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["scores"], a["stride"], a["nv"], a["rows"], a["nb"], a["k"], a["out"],
+                 a["cnt"], None)
+
+    assert call(rows=0) == pgqa.PGQA_OK                      # nothing to do, nothing launched
+    assert call(rows=-1) == pgqa.PGQA_ERR_SHAPE
+    assert call(k=-1) == pgqa.PGQA_ERR_SHAPE
+    assert call(nb=-1) == pgqa.PGQA_ERR_SHAPE
+    assert call(nb=pgqa.QSA_MAX_BLOCKS + 1, stride=pgqa.QSA_MAX_BLOCKS + 4) == pgqa.PGQA_ERR_SHAPE
+    assert call(k=pgqa.QSA_MAX_BLOCKS + 1) == pgqa.PGQA_ERR_SHAPE
+    assert call(scores=None) == pgqa.PGQA_ERR_NULL
+    assert call(out=None) == pgqa.PGQA_ERR_NULL
+    assert call(stride=63) == pgqa.PGQA_ERR_LAYOUT
+    assert call(scores=FAKE + 2) == pgqa.PGQA_ERR_LAYOUT
+    assert call(out=FAKE + 1) == pgqa.PGQA_ERR_LAYOUT
+    assert call(nv=FAKE + 3) == pgqa.PGQA_ERR_LAYOUT
+    assert call(cnt=FAKE + 2) == pgqa.PGQA_ERR_LAYOUT
+
+
+def test_topk_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define PGQA_QSA_MAX_BLOCKS (\d+)", text)
+    assert m and int(m.group(1)) == pgqa.QSA_MAX_BLOCKS
