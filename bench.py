@@ -73,6 +73,76 @@ def cpu_baseline(case, budget_s: float) -> dict:
             "sample": f"{n_calls} whole calls of the same workload, {per_call * 1e3:.1f} ms each"}
 
 
+def cpu_baseline_topk(case, budget_s: float) -> dict:
+    """The oracle's top-k selection, as it is, on a bounded sample of rows
+    (the first rows of the workload, doubling until about `budget_s`)."""
+    import oracle
+
+    rows, el = 16, 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.topk_select(case.scores[:rows], case.k, case.n_valid[:rows],
+                           n_blocks=case.n_blocks)
+        el = time.perf_counter() - t0
+        if el >= budget_s / 3 or rows >= case.rows:
+            break
+        rows = min(case.rows, rows * 2)
+    nv = case.n_valid[:rows].clip(0, case.n_blocks).astype("int64")
+    gbs = float(nv.sum()) * 4 / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {rows} of {case.rows} rows, {el * 1e3:.1f} ms"}
+
+
+def bench_topk(args) -> int:
+    """QSA top-k selection: one step = one qsa_topk_select call over every
+    row.  `value` is score-read GB/s: the eligible score bytes of all rows
+    (read once) divided by the average call time; the call is one kernel."""
+    import torch
+
+    from fp8_kv_amd import inputs, pgqa
+
+    pgqa.load()
+    torch.cuda.set_device(0)
+    case = inputs.topk_workload_case(args.workload)
+    R = max(1, args.pools)
+    scores = [torch.from_numpy(case.scores).to("cuda")]
+    for _ in range(R - 1):
+        scores.append(scores[0].clone())
+    nv = torch.from_numpy(case.n_valid).to("cuda")
+    idx = torch.empty((case.rows, case.k), dtype=torch.int32, device="cuda")
+    cnt = torch.empty(case.rows, dtype=torch.int32, device="cuda")
+
+    def call(i):
+        pgqa.qsa_topk_select(scores[i % R], case.k, nv, n_blocks=case.n_blocks, out_idx=idx,
+                             out_count=cnt)
+
+    ms = time_steps(call, args.steps, args.warmup, R, not args.eager)
+    score_bytes = case.score_bytes()
+    alg_bytes = score_bytes + case.rows * case.k * 4 + case.rows * 4
+    gbs = score_bytes / (ms * 1e-3) / 1e9
+    kernel_gbs = alg_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "score-read HBM GB/s and µs/call, QSA top-k block selection",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u32 keys of f32 scores",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "rows": case.rows, "n_blocks": case.n_blocks,
+                   "k": case.k, "pools_rotated": R, "us_per_call": round(ms * 1e3, 3),
+                   "score_bytes_per_call": score_bytes,
+                   "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "topk_kernel",
+                     "kernel_us": round(ms * 1e3, 3)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_topk(case, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def time_steps(step, steps: int, warmup: int, R: int, use_graph: bool) -> float:
     """Average milliseconds per step over exactly `steps` steps, timed with HIP
     events on the stream the kernels run on.  With use_graph the R steps of
@@ -133,9 +203,14 @@ def main() -> int:
               "multi-GPU path", file=sys.stderr)
         return 2
 
+    from fp8_kv_amd import inputs
+
+    if args.workload in inputs.TOPK_WORKLOADS:
+        return bench_topk(args)
+
     import torch
 
-    from fp8_kv_amd import inputs, pgqa
+    from fp8_kv_amd import pgqa
 
     pgqa.load()
     torch.cuda.set_device(0)

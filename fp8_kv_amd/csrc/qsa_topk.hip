@@ -11,25 +11,41 @@
 // u ^ (sign ? 0xFFFFFFFF : 0x80000000), which orders scores like IEEE 754
 // totalOrder (-NaN < -inf < ... < -0 < +0 < ... < +inf < +NaN).
 //
-// One workgroup of 1024 threads owns one row.  Thread t holds elements
-// j = 4096 i + 4 t + c (register slot i, component c) as keys in VGPRs, so a
-// row of up to 65,536 blocks is read from HBM exactly once.  The steps:
-//   1. T, a lower bound for the pivot: the k-th largest per-thread maximum
-//      (each of k threads owns a key >= T, so at least k keys are >= T).
-//      Skipped (T = 0) for rows that fit the candidate buffer.
-//   2. Keys >= T are appended to an LDS candidate buffer (about 1% of a row
-//      of independent scores when k is 1/128 of the row).
-//   3. Pivot P: four 8-bit MSB-first histogram passes over the candidates
-//      give the k-th largest key P and `need`, how many keys equal to P are
-//      kept.  If the candidates overflow the buffer the passes run over the
-//      register keys instead (same result, slower).
-//   4. Ordered output: per slot, wave ballots of (key > P) and (key == P)
-//      give each element its rank among greater-than and tied elements in
-//      index order; element j is kept if key > P or it is one of the first
-//      `need` ties, and lands at position (#greater before j) + min(#ties
-//      before j, need).
+// One workgroup of 1024 threads (16 waves) owns one row.  Thread t holds
+// elements j = 4096 i + 4 t + c (register slot i, component c) as raw fp32
+// bits in VGPRs, so a row of up to 65,536 blocks is read from HBM once, with
+// 16-byte coalesced loads.  Elements past the row's length hold -inf.
+//   1. Threshold T (rows longer than 4096 blocks, k <= 1024): each lane's
+//      maximum in key order (from max/min of the signed raw bits), then each
+//      wave's ceil(k/16)-th largest lane maximum by a 32-step ballot
+//      bisection, and T = the minimum over the 16 waves.  Every lane holds a
+//      full first slot, so every lane maximum is an eligible block and at
+//      least k keys are >= T.  Shorter rows take every eligible block.
+//   2. Candidates: blocks that are not below T as floats (a superset of the
+//      keys >= T) are appended, in one pass, to their wave's LDS region as
+//      (raw bits, block index) by ballot and mbcnt.  About 1.5% of a row of
+//      independent scores when k is 1/128 of the row.
+//   3. Pivot P, the k-th largest key: MSB-first 8-bit histogram passes over
+//      the candidates with key >= T, skipping the leading bytes that T and the
+//      row's largest key share (all such candidates share them).  Every wave
+//      scans the 256 bins itself, so a pass costs one barrier; three
+//      histogram buffers rotate.  `need` is how many keys equal to P are
+//      kept, `eq` how many there are.  The first pass checks that at least k
+//      candidates reach T and that no region overflowed; otherwise
+//      (adversarial inputs) four exact passes run over the whole row, re-read
+//      from cache.
+//   4. Kept blocks (key > P, or key >= P when every tie is kept) are marked in
+//      an LDS bitmap from the candidates; when eq > need the tied blocks go to
+//      a second bitmap of which a block-wide popcount scan keeps the first
+//      `need` in index order.  After the exact fallback the bitmaps come from
+//      a re-read of the row.
+//   5. Ordered output: thread t owns bitmap words 2t and 2t+1 (blocks 64t ..
+//      64t+63); a block-wide exclusive scan of their popcounts gives each
+//      thread its first output position, and it writes its blocks in order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "pgqa_internal.h"
 
@@ -39,48 +55,107 @@ namespace {
 constexpr int kThreads = kTopkThreads;
 constexpr int kWaves = kThreads / 64;
 constexpr int kSlotElems = 4 * kThreads;    // elements one register slot covers
-constexpr int kMaxItems = kTopkMaxBlocks / kSlotElems;
-constexpr int kCandCap = 8192;              // LDS candidate keys
+constexpr int kCandCap = 4096;              // LDS candidates (raw bits, block index)
+constexpr int kRegion = kCandCap / kWaves;  // per-wave candidate region
+constexpr int kThreshMin = kSlotElems;      // rows longer than this use a threshold
+constexpr int kBmWords = kTopkMaxBlocks / 32;
+constexpr uint32_t kNegInfBits = 0xFF800000u;
+static_assert(kBmWords == 2 * kThreads, "each thread owns two bitmap words");
 
 struct TopkShared {
-  uint32_t cand[kCandCap];
-  uint32_t tmax[kThreads];
-  uint32_t hist[2][256];
-  uint32_t gt_base[kMaxItems * kWaves];
-  uint32_t tie_base[kMaxItems * kWaves];
-  uint32_t n_cand;
-  uint32_t digit;
-  uint32_t cbefore;
+  uint2 cand[kCandCap];       // (raw score bits, block index)
+  uint32_t keep[kBmWords];    // bit j: block j is kept
+  uint32_t tied[kBmWords];    // bit j: block j's key equals the pivot (eq > need only)
+  uint32_t hist[3][256];
+  uint32_t twave[kWaves];
+  uint32_t tmax[kWaves];
+  uint32_t wsum[2][kWaves];
+  uint32_t gather[64];        // keys of the pivot's bin once it holds <= 64
+  uint32_t wcnt[kWaves];      // candidates per wave region
+  uint32_t result[4];         // pivot key, need, eq, ok (from wave 0)
 };
 
-__device__ __forceinline__ uint32_t key_of(float x) {
-  const uint32_t u = __float_as_uint(x);
+__device__ __forceinline__ uint32_t key_of_bits(uint32_t u) {
   return u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t bits_of_key(uint32_t k) {
+  return (k & 0x80000000u) ? (k ^ 0x80000000u) : ~k;
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// A copy of x the compiler cannot see through.  Each phase re-derives its
-// per-element compare masks from such a copy instead of keeping dozens of
-// 64-bit masks from an earlier phase alive across barriers.
-__device__ __forceinline__ int32_t fresh_v(int32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-__device__ __forceinline__ uint32_t fresh_s(uint32_t x) {
-  asm volatile("" : "+s"(x));
+// Inclusive prefix sum across the 64 lanes of a wave with DPP: a
+// Hillis-Steele scan inside each 16-lane row (row_shr 1, 2, 4, 8), then the
+// row totals carried across rows (row_bcast 15 into rows 1 and 3, row_bcast 31
+// into rows 2 and 3).  Lanes without a source lane add 0.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return x;
 }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  const int lane = lane_id();
+// Maximum across the 64 lanes of a wave (same DPP pattern as the scan; lanes
+// without a source lane see 0, the identity for unsigned max).
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false)));
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+// Exclusive prefix sum over the workgroup in thread order.  Contains a
+// barrier; `wsum` must not be in use by another scan in flight.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t c, uint32_t* wsum) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t incl = wave_incl_scan(c);
+  if (lane_id() == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
+  for (int w = 0; w < kWaves; ++w) base += w < wave ? wsum[w] : 0u;
+  return base + incl - c;
+}
+
+// The m-th largest (1 <= m <= 64) of the wave's 64 lane values, by bisection
+// on the bits from the top: at bit b, c lanes agree with the answer so far
+// and have bit b set; the answer has bit b set iff c >= m.
+__device__ __forceinline__ uint32_t wave_mth_largest(uint32_t x, uint32_t m) {
+  uint32_t res = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t trial = res | (1u << b);
+    const uint32_t c = static_cast<uint32_t>(__popcll(__ballot((x >> b) == (trial >> b))));
+    if (c >= m)
+      res = trial;
+    else
+      m -= c;
   }
-  return x;
+  return res;
+}
+
+// The m-th largest (1 <= m <= number of active lanes) of the active lanes'
+// values, all of which equal `prefix` above bit `bits`: bisection over the
+// low bits.
+__device__ __forceinline__ uint32_t wave_mth_largest_low(uint32_t x, bool act, uint32_t m,
+                                                         uint32_t prefix, int bits) {
+  uint32_t res = prefix;
+  for (int b = bits - 1; b >= 0; --b) {
+    const uint32_t trial = res | (1u << b);
+    const uint32_t c =
+        static_cast<uint32_t>(__popcll(__ballot(act && (x >> b) == (trial >> b))));
+    if (c >= m)
+      res = trial;
+    else
+      m -= c;
+  }
+  return res;
 }
 
 // Number of set bits of `mask` in lanes below this one.
@@ -89,71 +164,175 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
-// hist[d] += 1 for every active lane; one atomic per wave when all active
-// lanes share the digit (common in the first pass, where many scores share
-// an exponent).  Must be reached by the whole wave.
-__device__ __forceinline__ void hist_add(uint32_t* hist, bool act, uint32_t d) {
-  const uint64_t am = __ballot(act);
-  if (am == 0) return;
-  const int first = __ffsll(static_cast<unsigned long long>(am)) - 1;
-  const uint32_t d0 = __builtin_amdgcn_readlane(d, first);
-  const uint64_t same = __ballot(act && d == d0);
-  if (same == am) {
-    if (lane_id() == first) atomicAdd(&hist[d0], static_cast<uint32_t>(__popcll(am)));
-  } else if (act) {
-    atomicAdd(&hist[d], 1u);
-  }
-}
+struct Digit {
+  uint32_t digit;    // bin holding the rem-th largest key
+  uint32_t above;    // keys in higher bins
+  uint32_t in_bin;   // keys in that bin
+  uint32_t total;    // keys in all bins
+};
 
-// Wave 0: the digit whose bin holds the rem-th largest key (bins scanned from
-// 255 down), and the count of keys in higher bins.  Also clears the other
-// histogram buffer for the next pass.
-__device__ __forceinline__ void find_digit(TopkShared& sh, int buf, uint32_t rem) {
+// Every wave reads the 256 bins (lane l: bins 255-4l .. 252-4l) and finds the
+// bin holding the rem-th largest key, scanning from the top.  If the bins
+// hold fewer than rem keys, digit and above are 0.
+__device__ __forceinline__ Digit find_digit(const uint32_t* hist, uint32_t rem) {
   const int lane = lane_id();
-  uint32_t h[4];
-  uint32_t s = 0;
+  const uint4 v = *reinterpret_cast<const uint4*>(&hist[252 - 4 * lane]);
+  const uint32_t h[4] = {v.w, v.z, v.y, v.x};
+  const uint32_t s = h[0] + h[1] + h[2] + h[3];
+  const uint32_t incl = wave_incl_scan(s);
+  uint32_t c = incl - s;
+  bool found = false;
+  uint32_t fd = 0, fc = 0, fh = 0;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    h[m] = sh.hist[buf][255 - 4 * lane - m];
-    s += h[m];
-  }
-  uint32_t c = wave_incl_scan(s) - s;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    if (c < rem && rem <= c + h[m]) {
-      sh.digit = 255 - 4 * lane - m;
-      sh.cbefore = c;
+    if (!found && c < rem && rem <= c + h[m]) {
+      found = true;
+      fd = 255 - 4 * lane - m;
+      fc = c;
+      fh = h[m];
     }
     c += h[m];
   }
-#pragma unroll
-  for (int m = 0; m < 4; ++m) sh.hist[buf ^ 1][4 * lane + m] = 0;
+  const uint64_t fm = __ballot(found);
+  Digit r;
+  r.total = __builtin_amdgcn_readlane(incl, 63);
+  if (fm == 0) {
+    r.digit = r.above = r.in_bin = 0;
+  } else {
+    const int src = __ffsll(static_cast<unsigned long long>(fm)) - 1;
+    r.digit = __builtin_amdgcn_readlane(fd, src);
+    r.above = __builtin_amdgcn_readlane(fc, src);
+    r.in_bin = __builtin_amdgcn_readlane(fh, src);
+  }
+  return r;
 }
 
-// k-th largest key (k >= 1) of the multiset the visitor enumerates, and how
-// many keys equal to it rank within the first k (returned in *need).
-// Requires sh.hist[0] zeroed and a barrier since; leaves it zeroed again.
+struct Pivot {
+  uint32_t key;   // the k-th largest key
+  uint32_t need;  // keys equal to `key` among the first k
+  uint32_t eq;    // keys equal to `key` in the whole multiset
+  bool ok;        // the first pass saw at least k keys (and `accept` held)
+};
+
+// Block-wide pivot search: the k-th largest key of the multiset the visitor
+// enumerates (visit(f) calls f(act, key) with whole waves), four 8-bit
+// passes, one barrier each.  Requires hist[0] and hist[1] zeroed before a
+// barrier.  Used by the exact fallback over a whole row.
 template <class Visit>
-__device__ __forceinline__ uint32_t pivot_search(TopkShared& sh, uint32_t k, uint32_t* need,
-                                                 Visit visit) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__device__ __forceinline__ Pivot pivot_block(TopkShared& sh, uint32_t k, Visit visit) {
   uint32_t prefix = 0, rem = k;
+  Pivot pv{0, 0, 0, true};
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    uint32_t* hist = sh.hist[pass & 1];
+  for (int q = 0; q < 4; ++q) {
+    const int shift = 24 - 8 * q;
+    const uint32_t hi_mask = q == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    uint32_t* hist = sh.hist[q % 3];
     visit([&](bool act, uint32_t key) {
-      hist_add(hist, act && ((key ^ prefix) & hi_mask) == 0, (key >> shift) & 255u);
+      if (act && ((key ^ prefix) & hi_mask) == 0) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     });
     __syncthreads();
-    if (wave == 0) find_digit(sh, pass & 1, rem);
-    __syncthreads();
-    prefix |= __builtin_amdgcn_readfirstlane(sh.digit) << shift;
-    rem -= __builtin_amdgcn_readfirstlane(sh.cbefore);
+    // Zero the buffer of pass q + 2: every wave finished reading it (pass
+    // q - 1) before this barrier, and pass q + 2 adds to it only after the
+    // next one.
+    if (threadIdx.x < 256) sh.hist[(q + 2) % 3][threadIdx.x] = 0;
+    const Digit d = find_digit(hist, rem);
+    prefix |= d.digit << shift;
+    rem -= d.above;
+    pv.eq = d.in_bin;
   }
-  *need = rem;
-  return prefix;
+  pv.key = prefix;
+  pv.need = rem;
+  return pv;
+}
+
+// Orders this wave's LDS accesses: earlier ones complete before later ones
+// start (a single wave needs no barrier for its own LDS traffic).
+__device__ __forceinline__ void lds_fence_wave() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Single-wave pivot search over the per-wave candidate regions (keys >= T
+// count; all of them share the top `first` bytes of T).  MSB-first 8-bit
+// passes with the histogram in sh.hist[0]; once the pivot's bin holds at most
+// 64 keys they are gathered into lanes and a ballot bisection over the
+// remaining low bits finishes.  ok is false if a region overflowed or fewer
+// than k keys reach T.
+__device__ __forceinline__ Pivot pivot_wave(TopkShared& sh, uint32_t k, uint32_t T, int first) {
+  const int lane = lane_id();
+  Pivot pv{0, 0, 0, true};
+  uint32_t n[kWaves];
+  bool overflow = false;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    n[w] = __builtin_amdgcn_readfirstlane(sh.wcnt[w]);
+    overflow |= n[w] > static_cast<uint32_t>(kRegion);
+    n[w] = n[w] < static_cast<uint32_t>(kRegion) ? n[w] : kRegion;
+  }
+  // Visit every candidate key >= T: first chunk of each region unrolled so its
+  // reads are in flight together, the rest (regions over 64) in a loop.
+  auto visit = [&](auto f) {
+    uint32_t kx[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      kx[w] = static_cast<uint32_t>(lane) < n[w] ? sh.cand[kRegion * w + lane].x : 0u;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t key = key_of_bits(kx[w]);
+      f(static_cast<uint32_t>(lane) < n[w] && key >= T, key);
+    }
+    for (int w = 0; w < kWaves; ++w)
+      for (uint32_t b = 64; b < n[w]; b += 64) {
+        const uint32_t e = b + lane;
+        const uint32_t key = key_of_bits(e < n[w] ? sh.cand[kRegion * w + e].x : 0u);
+        f(e < n[w] && key >= T, key);
+      }
+  };
+  uint32_t prefix = first == 0 ? 0u : (T & (0xFFFFFFFFu << (32 - 8 * first)));
+  uint32_t rem = k;
+  uint32_t* hist = sh.hist[0];
+  for (int q = first; q < 4; ++q) {
+    const int shift = 24 - 8 * q;
+    const uint32_t hi_mask = q == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+#pragma unroll
+    for (int m = 0; m < 4; ++m) hist[4 * lane + m] = 0;
+    lds_fence_wave();
+    visit([&](bool act, uint32_t key) {
+      if (act && ((key ^ prefix) & hi_mask) == 0) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    });
+    lds_fence_wave();
+    const Digit d = find_digit(hist, rem);
+    if (q == first && (d.total < k || overflow)) {
+      pv.ok = false;
+      return pv;
+    }
+    prefix |= d.digit << shift;
+    rem -= d.above;
+    pv.eq = d.in_bin;
+    if (shift > 0 && d.in_bin <= 64) {
+      // Gather the pivot's bin into lanes and bisect its low `shift` bits.
+      const uint32_t lo_mask = 0xFFFFFFFFu << shift;
+      uint32_t got = 0;
+      visit([&](bool act, uint32_t key) {
+        const bool in = act && ((key ^ prefix) & lo_mask) == 0;
+        const uint64_t m = __ballot(in);
+        const uint32_t at = got + lanes_below(m);
+        if (in && at < 64) sh.gather[at] = key;
+        got += static_cast<uint32_t>(__popcll(m));
+      });
+      lds_fence_wave();
+      const bool act = static_cast<uint32_t>(lane) < d.in_bin;
+      const uint32_t key = act ? sh.gather[lane] : 0u;
+      const uint32_t P = wave_mth_largest_low(key, act, rem, prefix, shift);
+      pv.key = P;
+      pv.eq = static_cast<uint32_t>(__popcll(__ballot(act && key == P)));
+      pv.need = rem - static_cast<uint32_t>(__popcll(__ballot(act && key > P)));
+      return pv;
+    }
+  }
+  pv.key = prefix;
+  pv.need = rem;
+  return pv;
 }
 
 template <int ITEMS, bool VEC>
@@ -178,193 +357,231 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
     return;
   }
 
-  // ---- load the row's keys: element (i, c) of this thread is j = 4096 i + 4 tid + c,
-  // valid when 4096 i + c < lim.
+  // ---- load: element (i, c) of this thread is j = 4096 i + 4 tid + c, valid
+  // when 4096 i + c < lim.  Invalid elements hold -inf.
   const float* src = p.scores + static_cast<int64_t>(row) * p.row_stride;
   const int32_t lim = nv - 4 * tid;
-  uint32_t key[ITEMS][4];
+  uint32_t x[ITEMS][4];
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) key[i][c] = 0;
+    for (int c = 0; c < 4; ++c) x[i][c] = kNegInfBits;
     if (i * kSlotElems < nv) {
       if (VEC) {
         if (i * kSlotElems < lim) {
-          const float4 v =
-              *reinterpret_cast<const float4*>(src + i * kSlotElems + 4 * tid);
-          // Components past the row's length keep key 0: the per-thread
-          // maximum below must only see eligible blocks.
-          key[i][0] = key_of(v.x);
-          key[i][1] = i * kSlotElems + 1 < lim ? key_of(v.y) : 0u;
-          key[i][2] = i * kSlotElems + 2 < lim ? key_of(v.z) : 0u;
-          key[i][3] = i * kSlotElems + 3 < lim ? key_of(v.w) : 0u;
+          const uint4 v = *reinterpret_cast<const uint4*>(src + i * kSlotElems + 4 * tid);
+          x[i][0] = v.x;
+          if ((i + 1) * kSlotElems <= nv) {  // the whole slot is eligible
+            x[i][1] = v.y;
+            x[i][2] = v.z;
+            x[i][3] = v.w;
+          } else {
+            x[i][1] = i * kSlotElems + 1 < lim ? v.y : kNegInfBits;
+            x[i][2] = i * kSlotElems + 2 < lim ? v.z : kNegInfBits;
+            x[i][3] = i * kSlotElems + 3 < lim ? v.w : kNegInfBits;
+          }
         }
       } else {
+        // Uniform per-slot base, one lane offset for every slot; loads are
+        // unconditional (clamped into the row in the partial slot).
+        const uint32_t* sb = reinterpret_cast<const uint32_t*>(src) + i * kSlotElems;
+        if ((i + 1) * kSlotElems <= nv) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (i * kSlotElems + c < lim) key[i][c] = key_of(src[i * kSlotElems + 4 * tid + c]);
+          for (int c = 0; c < 4; ++c) x[i][c] = sb[4 * tid + c];
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const bool ok = i * kSlotElems + c < lim;
+            const uint32_t v = sb[ok ? 4 * tid + c : 0];
+            x[i][c] = ok ? v : kNegInfBits;
+          }
+        }
       }
     }
   }
 
-  // ---- 1. lower bound T from the per-thread maxima.  Rows longer than the
-  // candidate buffer give every thread at least one valid key (slot 0 is full).
-  const bool thresh = nv > kCandCap && k <= kThreads;
-  if (thresh) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) m = key[i][c] > m ? key[i][c] : m;  // invalid keys are 0
-    sh.tmax[tid] = m;
+  // Shared state for the phases below.
+  if (tid < 256) {
+    sh.hist[0][tid] = 0;
+    sh.hist[1][tid] = 0;
   }
-  if (tid < 256) sh.hist[0][tid] = 0;
-  if (tid == 0) sh.n_cand = 0;
-  __syncthreads();
-  uint32_t T = 0;
-  if (thresh) {
-    uint32_t unused;
-    T = pivot_search(sh, static_cast<uint32_t>(k), &unused, [&](auto f) {
-      f(true, sh.tmax[tid]);
-    });
-  }
+  sh.keep[2 * tid] = 0;
+  sh.keep[2 * tid + 1] = 0;
+  sh.tied[2 * tid] = 0;
+  sh.tied[2 * tid + 1] = 0;
 
-  // ---- 2. candidates (keys >= T) into LDS, wave-aggregated append.
-  uint32_t cnt = 0;
-  {
-    const int32_t l = fresh_v(lim);
-    const uint32_t t = fresh_s(T);
+
+  // ---- 1. threshold.  Rows longer than one slot give every thread a full
+  // first slot, so every lane maximum is an eligible block.  The lane maximum
+  // in key order: the largest signed raw value if any is non-negative, else
+  // the smallest (the negative score closest to zero).
+  const bool thresh = nv > kThreshMin && k <= kThreads;
+  if (thresh) {
+    int32_t mx = INT32_MIN, mn = INT32_MAX;
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) cnt += (i * kSlotElems + c < l && key[i][c] >= t) ? 1u : 0u;
+      for (int c = 0; c < 4; ++c) {
+        const int32_t v = static_cast<int32_t>(x[i][c]);
+        mx = v > mx ? v : mx;
+        mn = v < mn ? v : mn;
+      }
+    const uint32_t lane_max = key_of_bits(static_cast<uint32_t>(mx >= 0 ? mx : mn));
+    const uint32_t t_w =
+        wave_mth_largest(lane_max, (static_cast<uint32_t>(k) + kWaves - 1) / kWaves);
+    const uint32_t m_w = wave_max(lane_max);
+    if (lane == 0) {
+      sh.twave[wave] = t_w;
+      sh.tmax[wave] = m_w;
+    }
   }
-  const uint32_t incl = wave_incl_scan(cnt);
-  uint32_t base = 0;
-  if (lane == 63) base = atomicAdd(&sh.n_cand, incl);
-  base = __builtin_amdgcn_readlane(base, 63);
-  {
-    uint32_t pos = base + incl - cnt;
-    const int32_t l = fresh_v(lim);
-    const uint32_t t = fresh_s(T);
+  __syncthreads();
+  uint32_t T = 0, top = 0xFFFFFFFFu;
+  if (thresh) {
+    T = 0xFFFFFFFFu;
+    top = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      T = sh.twave[w] < T ? sh.twave[w] : T;
+      top = sh.tmax[w] > top ? sh.tmax[w] : top;
+    }
+    T = __builtin_amdgcn_readfirstlane(T);
+    top = __builtin_amdgcn_readfirstlane(top);
+  }
+  // A float test against T is a superset of the keys >= T (it also lets
+  // negative NaNs through) as long as T is a number above -inf, which keeps
+  // the -inf fillers out.
+  const bool float_cand = thresh && T >= 0x00800000u && T <= 0xFF800000u;
+
+  // ---- 2. candidates into this wave's region: (raw bits, block index).
+  uint32_t cnt = 0;  // this wave's candidates (wave-uniform)
+  auto append = [&](auto by_float) {
+    constexpr bool kFloat = decltype(by_float)::value;
+    uint2* region = sh.cand + kRegion * wave;
+    const float tf = __uint_as_float(bits_of_key(T));
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
       if (i * kSlotElems >= nv) break;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        if (i * kSlotElems + c < l && key[i][c] >= t) {
-          if (pos < kCandCap) sh.cand[pos] = key[i][c];
-          ++pos;
+        const bool cand = kFloat ? !(__uint_as_float(x[i][c]) < tf) : (i * kSlotElems + c < lim);
+        const uint64_t m = __ballot(cand);
+        if (m) {
+          const uint32_t at = cnt + lanes_below(m);
+          if (cand && at < static_cast<uint32_t>(kRegion))
+            region[at] = make_uint2(x[i][c], static_cast<uint32_t>(i * kSlotElems + 4 * tid + c));
+          cnt += static_cast<uint32_t>(__popcll(m));
         }
       }
     }
+  };
+  if (float_cand)
+    append(std::true_type{});
+  else
+    append(std::false_type{});
+  cnt = __builtin_amdgcn_readfirstlane(cnt);
+  if (lane == 0) sh.wcnt[wave] = cnt;
+  const uint32_t used = cnt < static_cast<uint32_t>(kRegion) ? cnt : kRegion;
+  const uint2* region = sh.cand + kRegion * wave;
+  __syncthreads();
+
+  // ---- 3. the pivot over the candidates with key >= T (wave 0).  Candidates
+  // with key in [T, top] share the leading bytes of T and top.
+  const uint32_t kk = static_cast<uint32_t>(k);
+  if (wave == 0) {
+    int first = 0;
+    if (float_cand) {
+      const uint32_t diff = T ^ top;
+      first = diff == 0 ? 3 : (__clz(diff) >> 3);
+    }
+    const Pivot w = pivot_wave(sh, kk, T, first);
+    if (lane == 0) {
+      sh.result[0] = w.key;
+      sh.result[1] = w.need;
+      sh.result[2] = w.eq;
+      sh.result[3] = w.ok ? 1u : 0u;
+    }
   }
   __syncthreads();
-  const uint32_t nc = __builtin_amdgcn_readfirstlane(sh.n_cand);
-
-  // ---- 3. the pivot.
-  uint32_t need = 0;
-  uint32_t P;
-  if (nc <= kCandCap) {
-    P = pivot_search(sh, static_cast<uint32_t>(k), &need, [&](auto f) {
-      for (uint32_t b = 0; b < nc; b += kThreads) {
-        const uint32_t e = b + tid;
-        f(e < nc, e < nc ? sh.cand[e] : 0u);
+  Pivot pv;
+  pv.key = __builtin_amdgcn_readfirstlane(sh.result[0]);
+  pv.need = __builtin_amdgcn_readfirstlane(sh.result[1]);
+  pv.eq = __builtin_amdgcn_readfirstlane(sh.result[2]);
+  const bool fast_pivot = __builtin_amdgcn_readfirstlane(sh.result[3]) != 0;
+  if (!fast_pivot) {
+    // Exact passes over the whole row, re-read from cache.  sh.hist[0] was
+    // last written by wave 0 before the barrier above.
+    if (tid < 256) {
+      sh.hist[0][tid] = 0;
+      sh.hist[1][tid] = 0;
+    }
+    __syncthreads();
+    pv = pivot_block(sh, kk, [&](auto f) {
+      for (int32_t b = 0; b < nv; b += kThreads) {
+        const int32_t j = b + tid;
+        f(j < nv, j < nv ? key_of_bits(__float_as_uint(src[j])) : 0u);
       }
     });
+  }
+  const uint32_t P = pv.key;
+  const bool split_ties = pv.eq != pv.need;  // only some of the pivot's ties are kept
+
+  // ---- 4. bitmaps of kept and (when only some are kept) tied blocks.
+  auto mark = [&](uint32_t key, uint32_t j) {
+    const uint32_t bit = 1u << (j & 31);
+    if (split_ties ? key > P : key >= P) atomicOr(&sh.keep[j >> 5], bit);
+    if (split_ties && key == P) atomicOr(&sh.tied[j >> 5], bit);
+  };
+  if (fast_pivot) {
+    // Every block with key >= P >= T is a candidate.
+    for (uint32_t b = 0; b < used; b += 64) {
+      const uint32_t e = b + lane;
+      if (e < used) {
+        const uint2 cj = region[e];
+        mark(key_of_bits(cj.x), cj.y);
+      }
+    }
   } else {
-    P = pivot_search(sh, static_cast<uint32_t>(k), &need, [&](auto f) {
-      const int32_t l = fresh_v(lim);
-      const uint32_t t = fresh_s(T);
-#pragma unroll
-      for (int i = 0; i < ITEMS; ++i) {
-        if (i * kSlotElems >= nv) break;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) f(i * kSlotElems + c < l && key[i][c] >= t, key[i][c]);
-      }
-    });
+    for (int32_t b = 0; b < nv; b += kThreads) {
+      const int32_t j = b + tid;
+      if (j < nv) mark(key_of_bits(__float_as_uint(src[j])), static_cast<uint32_t>(j));
+    }
+  }
+  __syncthreads();
+  uint32_t w0 = sh.keep[2 * tid];
+  uint32_t w1 = sh.keep[2 * tid + 1];
+  if (split_ties) {
+    // Keep the first `need` tied blocks in index order.
+    uint32_t q0 = sh.tied[2 * tid];
+    uint32_t q1 = sh.tied[2 * tid + 1];
+    const uint32_t qc = __popc(q0) + __popc(q1);
+    const uint32_t before = block_excl_scan(qc, sh.wsum[0]);
+    uint32_t take = before < pv.need ? pv.need - before : 0u;
+    while (take > 0 && q0) {
+      w0 |= q0 & (0u - q0);
+      q0 &= q0 - 1u;
+      --take;
+    }
+    while (take > 0 && q1) {
+      w1 |= q1 & (0u - q1);
+      q1 &= q1 - 1u;
+      --take;
+    }
   }
 
-  // ---- 4. ordered output.  Per (slot, wave) counts of greater and tied keys.
-  {
-    const int32_t lim4 = fresh_v(lim);
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      uint32_t g = 0, q = 0;
-      if (i * kSlotElems < nv) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bool v = i * kSlotElems + c < lim4;
-          g += __popcll(__ballot(v && key[i][c] > P));
-          q += __popcll(__ballot(v && key[i][c] == P));
-        }
-      }
-      if (lane == 0) {
-        sh.gt_base[i * kWaves + wave] = g;
-        sh.tie_base[i * kWaves + wave] = q;
-      }
-    }
+  // ---- 5. ordered output of blocks 64 tid .. 64 tid + 63.
+  uint32_t pos = block_excl_scan(__popc(w0) + __popc(w1), sh.wsum[1]);
+  while (w0) {
+    const int b = __ffs(w0) - 1;
+    if (pos < kk) out[pos] = 64 * tid + b;
+    ++pos;
+    w0 &= w0 - 1u;
   }
-  __syncthreads();
-  if (wave == 0) {  // exclusive scan over (slot, wave) in index order
-    constexpr int E = ITEMS * kWaves;
-    constexpr int PER = (E + 63) / 64;
-    uint32_t gv[PER], tv[PER], gs = 0, ts = 0;
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int e = lane * PER + m;
-      gv[m] = e < E ? sh.gt_base[e] : 0u;
-      tv[m] = e < E ? sh.tie_base[e] : 0u;
-      gs += gv[m];
-      ts += tv[m];
-    }
-    uint32_t ge = wave_incl_scan(gs) - gs;
-    uint32_t te = wave_incl_scan(ts) - ts;
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int e = lane * PER + m;
-      if (e < E) {
-        sh.gt_base[e] = ge;
-        sh.tie_base[e] = te;
-      }
-      ge += gv[m];
-      te += tv[m];
-    }
-  }
-  __syncthreads();
-  const int32_t lim5 = fresh_v(lim);
-  const uint32_t P5 = fresh_s(P);
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    if (i * kSlotElems >= nv) break;
-    bool gt[4], eq[4];
-    uint64_t gm[4], tm[4];
-    uint64_t any = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bool v = i * kSlotElems + c < lim5;
-      gt[c] = v && key[i][c] > P5;
-      eq[c] = v && key[i][c] == P5;
-      gm[c] = __ballot(gt[c]);
-      tm[c] = __ballot(eq[c]);
-      any |= gm[c] | tm[c];
-    }
-    if (any == 0) continue;
-    uint32_t gb = sh.gt_base[i * kWaves + wave];
-    uint32_t tb = sh.tie_base[i * kWaves + wave];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      gb += lanes_below(gm[c]);
-      tb += lanes_below(tm[c]);
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t at = gb + (tb < need ? tb : need);
-      if ((gt[c] || (eq[c] && tb < need)) && at < static_cast<uint32_t>(k))
-        out[at] = i * kSlotElems + 4 * tid + c;
-      gb += gt[c] ? 1u : 0u;
-      tb += eq[c] ? 1u : 0u;
-    }
+  while (w1) {
+    const int b = __ffs(w1) - 1;
+    if (pos < kk) out[pos] = 64 * tid + 32 + b;
+    ++pos;
+    w1 &= w1 - 1u;
   }
   if (tid == 0 && p.out_count) p.out_count[row] = k;
 }
