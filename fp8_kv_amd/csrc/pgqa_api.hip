@@ -178,7 +178,7 @@ int plan_call(int32_t n, int32_t hkv, int32_t max_len, int32_t num_splits, Split
 int run_attention(const void* q, const pgqa_kv_pool* kv, const int32_t* table, int32_t max_pages,
                   const int32_t* lens, int32_t max_len, int32_t n, int32_t hq, int32_t hkv,
                   int32_t head_dim, float sm_scale, int32_t num_splits, void* out,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+                  void* workspace, size_t workspace_bytes, void* stream, bool stream_kv) {
   int rc = validate_call(q, kv, table, max_pages, lens, max_len, n, hq, hkv, head_dim, sm_scale,
                          num_splits, out);
   if (rc != PGQA_OK || n == 0) return rc;
@@ -194,6 +194,7 @@ int run_attention(const void* q, const pgqa_kv_pool* kv, const int32_t* table, i
                                    plan);
   p.out = static_cast<uint16_t*>(out);
   p.partials = plan.splits > 1;
+  p.stream_kv = stream_kv;
   if (p.partials) {
     p.ws_o = static_cast<float*>(workspace);
     p.ws_lse = p.ws_o + static_cast<size_t>(n) * hq * plan.splits * kHeadDim;
@@ -238,7 +239,9 @@ int paged_gqa_decode(const void* q, const pgqa_kv_pool* kv, const int32_t* page_
                      void* workspace, size_t workspace_bytes, void* stream) {
   return run_attention(q, kv, page_table, max_pages, seq_lens, max_seq_len, batch, num_q_heads,
                        num_kv_heads, head_dim, sm_scale, num_splits, out, workspace,
-                       workspace_bytes, stream);
+                       workspace_bytes, stream,
+                       // Each K/V byte is read once per call: non-temporal loads.
+                       /*stream_kv=*/true);
 }
 
 int paged_gqa_prefill_sparse(const void* q, const pgqa_kv_pool* kv, const int32_t* row_tables,
@@ -248,7 +251,10 @@ int paged_gqa_prefill_sparse(const void* q, const pgqa_kv_pool* kv, const int32_
                              void* workspace, size_t workspace_bytes, void* stream) {
   return run_attention(q, kv, row_tables, max_pages, row_lens, max_row_len, rows, num_q_heads,
                        num_kv_heads, head_dim, sm_scale, num_splits, out, workspace,
-                       workspace_bytes, stream);
+                       workspace_bytes, stream,
+                       // Rows share one pool and re-read it through the caches: normal
+                       // loads (non-temporal ones measured 23% slower on 4096 rows).
+                       /*stream_kv=*/false);
 }
 
 int paged_gqa_decode_partial(const void* q, const pgqa_kv_pool* kv, const int32_t* page_table,
@@ -268,6 +274,7 @@ int paged_gqa_decode_partial(const void* q, const pgqa_kv_pool* kv, const int32_
   pgqa::AttnParams p = make_params(q, kv, page_table, max_pages, seq_lens, max_seq_len, batch,
                                    num_q_heads, num_kv_heads, sm_scale, plan);
   p.partials = true;
+  p.stream_kv = true;
   p.ws_o = part_o;
   p.ws_lse = part_lse;
   return pgqa::launch_attention(p, kv->kv_dtype == PGQA_KV_E4M3,
@@ -293,37 +300,6 @@ int e4m3_decode_table(float* out256, void* stream) {
   return pgqa::launch_e4m3_table(out256, static_cast<hipStream_t>(stream)) == hipSuccess
              ? PGQA_OK
              : PGQA_ERR_HIP;
-}
-
-int qsa_topk_select(const float* scores, int64_t row_stride, const int32_t* n_valid,
-                    int32_t rows, int32_t n_blocks, int32_t k, int32_t* out_idx,
-                    int32_t* out_count, void* stream) {
-  static_assert(PGQA_QSA_MAX_BLOCKS == pgqa::kTopkMaxBlocks, "block limit mismatch");
-  if (rows < 0 || k < 0 || n_blocks < 0 || n_blocks > PGQA_QSA_MAX_BLOCKS ||
-      k > PGQA_QSA_MAX_BLOCKS)
-    return PGQA_ERR_SHAPE;
-  if (rows == 0) return PGQA_OK;
-  if (!scores || (k > 0 && !out_idx)) return PGQA_ERR_NULL;
-  if (row_stride < n_blocks || row_stride < 0) return PGQA_ERR_LAYOUT;
-  const auto misaligned4 = [](const void* ptr) {
-    return (reinterpret_cast<uintptr_t>(ptr) & 3u) != 0;
-  };
-  if (misaligned4(scores) || misaligned4(out_idx) || misaligned4(n_valid) ||
-      misaligned4(out_count))
-    return PGQA_ERR_LAYOUT;
-  pgqa::TopkParams p;
-  p.scores = scores;
-  p.row_stride = row_stride;
-  p.n_valid = n_valid;
-  p.rows = rows;
-  p.n_blocks = n_blocks;
-  p.k = k;
-  p.out_idx = out_idx;
-  p.out_count = out_count;
-  const bool vec = aligned16(scores) && row_stride % 4 == 0 && n_blocks % 4 == 0;
-  if (pgqa::launch_topk(p, vec, static_cast<hipStream_t>(stream)) != hipSuccess)
-    return PGQA_ERR_HIP;
-  return PGQA_OK;
 }
 
 const char* pgqa_error_string(int code) {

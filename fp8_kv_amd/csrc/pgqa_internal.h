@@ -37,6 +37,7 @@ struct AttnParams {
   int32_t chunk;           // tokens per split, multiple of kTile * waves
   int32_t waves;           // waves per workgroup: 4 or 8
   bool partials;           // write split partials (ws_o, ws_lse) instead of out
+  bool stream_kv;          // non-temporal K/V loads (each byte read once per call)
   uint16_t* out;           // fp16 bits [n][hq][256]
   float* ws_o;             // [n*hq][splits][256] split outputs (v_scale applied)
   float* ws_lse;           // [n*hq][splits] base-2 log-sum-exp, -inf if empty
@@ -51,26 +52,9 @@ struct MergeParams {
   uint16_t* out;           // fp16 bits [rows][256]
 };
 
-// QSA top-k block selection (qsa_topk.hip): one workgroup per row.
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkMaxBlocks = 65536;   // blocks per row held in registers
-
-struct TopkParams {
-  const float* scores;     // [rows][row_stride]
-  int64_t row_stride;      // elements
-  const int32_t* n_valid;  // [rows] or nullptr (= n_blocks)
-  int32_t rows;
-  int32_t n_blocks;        // <= kTopkMaxBlocks
-  int32_t k;
-  int32_t* out_idx;        // [rows][k]
-  int32_t* out_count;      // [rows] or nullptr
-};
-
 hipError_t launch_attention(const AttnParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_e4m3_table(float* out256, hipStream_t stream);
 size_t attention_lds_bytes(int group, int waves);
-// vec: scores 16-byte aligned, row_stride and n_blocks multiples of 4.
-hipError_t launch_topk(const TopkParams& p, bool vec, hipStream_t stream);
 
 }  // namespace pgqa

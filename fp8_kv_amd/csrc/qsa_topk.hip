@@ -47,9 +47,9 @@
 
 #include <type_traits>
 
-#include "pgqa_internal.h"
+#include "qsa_internal.h"
 
-namespace pgqa {
+namespace qsa {
 namespace {
 
 constexpr int kThreads = kTopkThreads;
@@ -607,4 +607,4 @@ hipError_t launch_topk(const TopkParams& p, bool vec, hipStream_t stream) {
   return launch_items<16>(p, vec, stream);
 }
 
-}  // namespace pgqa
+}  // namespace qsa

@@ -8,6 +8,11 @@ from .oracle import (  # noqa: F401
     ORACLE_ERR_ARG,
     ORACLE_ERR_PAGE,
     ORACLE_ERR_TABLE,
+    PAGE4_EMPTY,
+    PAGE4_OVERFLOW,
+    PAGE4_PAGE,
+    PAGE4_PARTIAL,
+    PAGE4_TAIL,
     OracleError,
     build,
     e4m3_table,
@@ -16,5 +21,6 @@ from .oracle import (  # noqa: F401
     load,
     num_threads,
     paged_gqa,
+    qsa_page4_table,
     topk_select,
 )

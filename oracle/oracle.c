@@ -288,3 +288,121 @@ int oracle_topk_select(const float* scores, int64_t row_stride, const int32_t* n
   }
   return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * Virtual page-4 table of a QSA selection ("[Kernel][SM70] Accelerate Qwen3.8
+ * QSA paged prefill", Purpose and Changes: each four-token selection becomes
+ * a zero-copy page of a page-4 view of the KV pool; the page-4 pages are
+ * sorted for locality; the causal partial page goes last and is checked
+ * against the expanded selection; positions past the live length are clamped
+ * away and invalid rows are made inert).
+ *
+ * Definition, per row r (L = live_len[r], s = row_seq ? row_seq[r] : 0):
+ *   L <= 0: the row is inert (status EMPTY).
+ *   S = { t in tokens[r] : 0 <= t < L } as a set (duplicates and stale or
+ *       padded positions drop out).
+ *   c = (L - 1) / 4, the 4-token block holding the row's own position.
+ *   Full pages: blocks b < c with all of 4b .. 4b+3 in S.  Any other token
+ *       of S below 4c makes the row PARTIAL.
+ *   Causal page: T = S ∩ [4c, L), n_tail = |T|; T must be 4c .. 4c+n_tail-1
+ *       (else TAIL).
+ *   The virtual page-4 id of block b: the physical page
+ *       p = block_table[s][4b / P] must exist (4b / P < max_pages) and lie in
+ *       [0, num_pages) (else PAGE); id = p * vpages_per_page + (4b mod P) / 4.
+ *   More than out_stride pages: OVERFLOW.
+ *   Output row: the full pages' ids ascending, then the causal page's id if
+ *       n_tail > 0, then -1; out_len = 4 * n_full + n_tail.  A row with any
+ *       status bit set is inert: all -1 and out_len 0.
+ * Status bits are ORed (EMPTY alone when L <= 0).
+ * --------------------------------------------------------------------------- */
+#define PAGE4_EMPTY 1
+#define PAGE4_PARTIAL 2
+#define PAGE4_TAIL 4
+#define PAGE4_PAGE 8
+#define PAGE4_OVERFLOW 16
+
+int oracle_qsa_page4_table(const int32_t* tokens, int64_t token_stride, int32_t n_tokens,
+                           const int32_t* live_len, const int32_t* block_table,
+                           int32_t max_pages, const int32_t* row_seq, int32_t num_pages,
+                           int32_t page_size, int32_t vpages_per_page, int32_t rows,
+                           int32_t* out_table, int32_t out_stride, int32_t* out_len,
+                           int32_t* out_status) {
+  if (!tokens || !live_len || !block_table || !out_table || !out_len || !out_status ||
+      rows < 0 || n_tokens < 0 || token_stride < n_tokens || max_pages < 1 ||
+      page_size < 4 || page_size % 4 != 0 || vpages_per_page < page_size / 4 ||
+      out_stride < 1 || num_pages < 0)
+    return ORACLE_ERR_ARG;
+  int failed = 0;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int32_t r = 0; r < rows; ++r) {
+    int32_t* orow = out_table + (int64_t)r * out_stride;
+    for (int32_t i = 0; i < out_stride; ++i) orow[i] = -1;
+    out_len[r] = 0;
+    const int32_t L = live_len[r];
+    if (L <= 0) {
+      out_status[r] = PAGE4_EMPTY;
+      continue;
+    }
+    /* S: the live selected positions, sorted, duplicates removed. */
+    int32_t* set = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n_tokens > 0 ? n_tokens : 1));
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n_tokens / 4 + 1));
+    if (!set || !ids) {
+      free(set);
+      free(ids);
+#pragma omp atomic write
+      failed = 1;
+      continue;
+    }
+    const int32_t* trow = tokens + (int64_t)r * token_stride;
+    int32_t m = 0;
+    for (int32_t i = 0; i < n_tokens; ++i)
+      if (trow[i] >= 0 && trow[i] < L) set[m++] = trow[i];
+    qsort(set, (size_t)m, sizeof(int32_t), cmp_int);
+    int32_t u = 0;
+    for (int32_t i = 0; i < m; ++i)
+      if (u == 0 || set[i] != set[u - 1]) set[u++] = set[i];
+    m = u;
+
+    const int32_t c = (L - 1) / 4;
+    const int32_t seq = row_seq ? row_seq[r] : 0;
+    const int32_t* btab = block_table + (int64_t)seq * max_pages;
+    int status = 0, n_full = 0, below = 0, n_tail = 0;
+    /* Walk S in order: whole blocks below c become pages. */
+    int32_t i = 0;
+    while (i < m && set[i] < 4 * c) {
+      const int32_t b = set[i] / 4;
+      int32_t j = i;
+      while (j < m && set[j] / 4 == b) ++j;
+      if (j - i == 4) ids[n_full++] = b; /* four distinct tokens of one block: all of it */
+      below += j - i;
+      i = j;
+    }
+    if (below != 4 * n_full) status |= PAGE4_PARTIAL;
+    n_tail = m - i; /* the tokens of S in [4c, L) */
+    if (n_tail > 0 && set[m - 1] != 4 * c + n_tail - 1) status |= PAGE4_TAIL;
+    const int32_t n_pages = n_full + (n_tail > 0 ? 1 : 0);
+    if (n_pages > out_stride) status |= PAGE4_OVERFLOW;
+    if (n_tail > 0) ids[n_full] = c;
+    /* Logical block -> virtual page-4 id through the physical block table. */
+    for (int32_t k = 0; k < n_pages; ++k) {
+      const int32_t b = ids[k];
+      const int64_t lp = (int64_t)b * 4 / page_size;
+      const int32_t p = lp < max_pages ? btab[lp] : -1;
+      if (p < 0 || p >= num_pages) {
+        status |= PAGE4_PAGE;
+        ids[k] = -1;
+      } else {
+        ids[k] = p * vpages_per_page + (int32_t)(((int64_t)b * 4 % page_size) / 4);
+      }
+    }
+    out_status[r] = status;
+    if (status == 0) {
+      qsort(ids, (size_t)n_full, sizeof(int32_t), cmp_int); /* locality order */
+      for (int32_t k = 0; k < n_pages; ++k) orow[k] = ids[k];
+      out_len[r] = 4 * n_full + n_tail;
+    }
+    free(set);
+    free(ids);
+  }
+  return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}

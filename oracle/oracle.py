@@ -20,6 +20,13 @@ ORACLE_ERR_ARG = -1
 ORACLE_ERR_PAGE = -2
 ORACLE_ERR_TABLE = -3
 
+# Row status bits of the page-4 table builder (see oracle.c).
+PAGE4_EMPTY = 1
+PAGE4_PARTIAL = 2
+PAGE4_TAIL = 4
+PAGE4_PAGE = 8
+PAGE4_OVERFLOW = 16
+
 
 class OracleError(RuntimeError):
     def __init__(self, code: int):
@@ -75,6 +82,11 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.oracle_topk_select.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_void_p, ctypes.c_void_p]
+    lib.oracle_qsa_page4_table.restype = ctypes.c_int
+    lib.oracle_qsa_page4_table.argtypes = [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     _lib_cache[path] = lib
     return lib
 
@@ -165,3 +177,37 @@ def topk_select(scores: np.ndarray, k: int, n_valid=None, n_blocks: int | None =
     if rc != 0:
         raise OracleError(rc)
     return idx, cnt
+
+
+def qsa_page4_table(tokens: np.ndarray, live_len, block_table: np.ndarray, *, num_pages: int,
+                    page_size: int, vpages_per_page: int, out_stride: int, row_seq=None,
+                    lib_path: str = _LIB):
+    """Virtual page-4 table of each row's expanded QSA selection (see
+    oracle.c).  tokens: int32 [rows][n_tokens] logical positions (-1 =
+    padding); live_len: int32 [rows]; block_table: int32 [n_seqs][max_pages]
+    physical page of each logical page of `page_size` tokens; row_seq: int32
+    [rows] or None (all rows in sequence 0).  Returns (table int32
+    [rows][out_stride], lens int32 [rows], status int32 [rows])."""
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    if tokens.ndim != 2:
+        raise ValueError("tokens must be [rows][n_tokens]")
+    rows, n_tok = tokens.shape
+    live = np.ascontiguousarray(live_len, dtype=np.int32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    if bt.ndim == 1:
+        bt = bt[None, :]
+    seq = None if row_seq is None else np.ascontiguousarray(row_seq, dtype=np.int32)
+    if live.shape != (rows,) or (seq is not None and seq.shape != (rows,)):
+        raise ValueError("live_len and row_seq must be [rows]")
+    if seq is not None and rows and (seq.min() < 0 or seq.max() >= bt.shape[0]):
+        raise ValueError("row_seq names a sequence outside block_table")
+    table = np.empty((rows, out_stride), dtype=np.int32)
+    lens = np.empty(rows, dtype=np.int32)
+    status = np.empty(rows, dtype=np.int32)
+    rc = load(lib_path).oracle_qsa_page4_table(
+        tokens.ctypes.data, n_tok, n_tok, live.ctypes.data, bt.ctypes.data, bt.shape[1],
+        None if seq is None else seq.ctypes.data, num_pages, page_size, vpages_per_page, rows,
+        table.ctypes.data, out_stride, lens.ctypes.data, status.ctypes.data)
+    if rc != 0:
+        raise OracleError(rc)
+    return table, lens, status
