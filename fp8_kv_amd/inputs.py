@@ -378,3 +378,140 @@ def topk_workload_case(name: str, **overrides) -> TopkCase:
     kw = dict(TOPK_WORKLOADS[name])
     kw.update(overrides)
     return topk_case(**kw)
+
+
+@dataclass
+class Page4Case:
+    """Expanded QSA selections of query rows ("[Kernel][SM70] Accelerate
+    Qwen3.8 QSA paged prefill", Changes): row r's selection lists logical token
+    positions of its sequence, four per selected 4-token block plus the
+    selected tokens of its own (causal) block; the sequence's tokens live in
+    physical pages of `page_size` tokens named by a block table."""
+    tokens: np.ndarray            # int32 [rows][n_tokens], -1 = padding
+    live_len: np.ndarray          # int32 [rows]
+    block_table: np.ndarray       # int32 [n_seqs][max_pages]
+    row_seq: np.ndarray | None    # int32 [rows] or None (every row in sequence 0)
+    num_pages: int                # physical pages in the pool
+    page_size: int                # tokens per physical page (a multiple of 4)
+    vpages_per_page: int          # page-4 views per physical page: page_stride / (4 token_stride)
+    out_stride: int               # entries per output table row
+    kv: PagedCase | None = None   # q and the physical pool (with_kv only)
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def rows(self) -> int:
+        return int(self.tokens.shape[0])
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.tokens.shape[1])
+
+    def builder_kwargs(self) -> dict:
+        return dict(num_pages=self.num_pages, page_size=self.page_size,
+                    vpages_per_page=self.vpages_per_page, out_stride=self.out_stride,
+                    row_seq=self.row_seq)
+
+
+def page4_selection_case(*, rows: int, selected_blocks: int, tail: int, seq_blocks: int,
+                         page_size: int = 16, live_tail: int | None = None,
+                         order: str = "expanded", layout: str = "interleaved", seed: int = 0,
+                         pad: int = 0, out_stride: int | None = None, with_kv: bool = False,
+                         kv_dtype: int = KV_FP16, num_q_heads: int = 6, num_kv_heads: int = 1,
+                         head_dim: int = 256) -> Page4Case:
+    """Selections of `rows` query rows of one sequence of 4*seq_blocks tokens.
+
+    Row r's causal block is c_r = seq_blocks - rows + r and its live length
+    4*c_r + live_tail (live_tail in 1..4, default max(tail, 1)).  It selects
+    `selected_blocks` distinct blocks drawn uniformly from [0, c_r) plus the
+    first `tail` (0..live_tail) tokens of block c_r.
+    order: "expanded" (blocks ascending, each as 4b..4b+3, then the causal
+    tokens), "blocks" (the blocks in random order, each expanded), or
+    "shuffled" (every token position in random order).  `pad` entries of -1
+    follow.  The block table is a random permutation of the sequence's
+    physical pages (nonmonotonic).  Seeds: SeedSequence(seed).spawn(6) children
+    for q, K, V, the block table, the selections and the orders.
+    """
+    P = page_size
+    live_tail = max(tail, 1) if live_tail is None else live_tail
+    assert P % 4 == 0 and (4 * seq_blocks) % P == 0
+    assert 1 <= live_tail <= 4 and 0 <= tail <= live_tail
+    assert seq_blocks - rows >= selected_blocks and rows >= 1
+    num_pages = 4 * seq_blocks // P
+    ss = np.random.SeedSequence(seed).spawn(6)
+    rq, rk, rv, rt, rsel, rord = (np.random.default_rng(s) for s in ss)
+    btab = rt.permutation(num_pages).astype(np.int32)[None, :]
+    n_tok = 4 * selected_blocks + tail + pad
+    tokens = np.full((rows, n_tok), -1, dtype=np.int32)
+    live = np.empty(rows, dtype=np.int32)
+    quad = np.arange(4, dtype=np.int64)
+    for r in range(rows):
+        c_r = seq_blocks - rows + r
+        live[r] = 4 * c_r + live_tail
+        blocks = rsel.choice(c_r, size=selected_blocks, replace=False, shuffle=False)
+        if order == "expanded":
+            blocks = np.sort(blocks)
+        elif order in ("blocks", "shuffled"):
+            blocks = rord.permutation(blocks)
+        else:
+            raise ValueError(order)
+        toks = np.concatenate([(4 * blocks.astype(np.int64)[:, None] + quad).reshape(-1),
+                               4 * c_r + np.arange(tail, dtype=np.int64)])
+        if order == "shuffled":
+            toks = rord.permutation(toks)
+        tokens[r, :toks.size] = toks
+    if out_stride is None:
+        out_stride = selected_blocks + 1
+    ts = num_kv_heads * head_dim
+    kv = None
+    if with_kv:
+        q = rq.standard_normal((rows, num_q_heads, head_dim), dtype=np.float32).astype(np.float16)
+        shape = (num_pages, P, num_kv_heads, head_dim)
+        pool = build_pool(_values(rk, shape, kv_dtype), _values(rv, shape, kv_dtype), layout)
+        ts = pool["token_stride"]
+        kv = PagedCase(q=q, **pool, num_pages=num_pages, page_size=P, kv_dtype=kv_dtype,
+                       k_scale=1.0, v_scale=1.0, table=btab, lens=live.copy(),
+                       max_seq_len=int(live.max()), sm_scale=1.0 / np.sqrt(head_dim),
+                       num_kv_heads=num_kv_heads, layout=layout)
+        page_stride = pool["page_stride"]
+    else:
+        page_stride = (2 if layout == "interleaved" else 1) * P * ts
+    assert page_stride % (4 * ts) == 0
+    return Page4Case(tokens=tokens, live_len=live, block_table=btab, row_seq=None,
+                     num_pages=num_pages, page_size=P,
+                     vpages_per_page=page_stride // (4 * ts), out_stride=out_stride, kv=kv,
+                     meta=dict(selected_blocks=selected_blocks, tail=tail, order=order,
+                               seed=seed, layout=layout))
+
+
+def page4_view(kv: PagedCase, table: np.ndarray, lens: np.ndarray) -> PagedCase:
+    """The same physical pool read as pages of 4 tokens: page i of the view
+    starts at element i * 4 * token_stride of the pool (so a view id is
+    physical page * page_stride / (4 token_stride) + slot / 4), with the
+    given per-row tables and lengths."""
+    ts = kv.token_stride
+    assert kv.page_stride % (4 * ts) == 0
+    vpp = kv.page_stride // (4 * ts)
+    return PagedCase(q=kv.q, k_store=kv.k_store, v_store=kv.v_store, k_offset=kv.k_offset,
+                     v_offset=kv.v_offset, page_stride=4 * ts, token_stride=ts,
+                     head_stride=kv.head_stride, num_pages=kv.num_pages * vpp, page_size=4,
+                     kv_dtype=kv.kv_dtype, k_scale=kv.k_scale, v_scale=kv.v_scale,
+                     table=np.ascontiguousarray(table, dtype=np.int32),
+                     lens=np.ascontiguousarray(lens, dtype=np.int32),
+                     max_seq_len=max(1, int(np.max(lens, initial=0))), sm_scale=kv.sm_scale,
+                     num_kv_heads=kv.num_kv_heads, layout=kv.layout + "/page4-view")
+
+
+# Page-4 table building for the sparse-prefill workload's shape: 4096 rows,
+# 512 selected blocks plus 3 causal tokens each (2051 tokens), one sequence of
+# 262,144 tokens in physical pages of 16 tokens, interleaved K/V.
+PAGE4_WORKLOADS = {
+    "qsa_page4_table_4096x2051_p16": dict(rows=4096, selected_blocks=512, tail=3,
+                                          seq_blocks=65536, page_size=16, order="blocks",
+                                          layout="interleaved", seed=81),
+}
+
+
+def page4_workload_case(name: str, **overrides) -> Page4Case:
+    kw = dict(PAGE4_WORKLOADS[name])
+    kw.update(overrides)
+    return page4_selection_case(**kw)

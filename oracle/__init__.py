@@ -9,9 +9,12 @@ from .oracle import (  # noqa: F401
     ORACLE_ERR_PAGE,
     ORACLE_ERR_TABLE,
     PAGE4_EMPTY,
+    PAGE4_LONG,
+    PAGE4_MAX_LIVE,
     PAGE4_OVERFLOW,
     PAGE4_PAGE,
     PAGE4_PARTIAL,
+    PAGE4_SEQ,
     PAGE4_TAIL,
     OracleError,
     build,

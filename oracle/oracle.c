@@ -298,7 +298,8 @@ int oracle_topk_select(const float* scores, int64_t row_stride, const int32_t* n
  * away and invalid rows are made inert).
  *
  * Definition, per row r (L = live_len[r], s = row_seq ? row_seq[r] : 0):
- *   L <= 0: the row is inert (status EMPTY).
+ *   L <= 0: the row is inert (status EMPTY); L > 2^26: inert (status LONG).
+ *   s outside [0, n_seqs): no block table to read (status SEQ).
  *   S = { t in tokens[r] : 0 <= t < L } as a set (duplicates and stale or
  *       padded positions drop out).
  *   c = (L - 1) / 4, the 4-token block holding the row's own position.
@@ -313,24 +314,28 @@ int oracle_topk_select(const float* scores, int64_t row_stride, const int32_t* n
  *   Output row: the full pages' ids ascending, then the causal page's id if
  *       n_tail > 0, then -1; out_len = 4 * n_full + n_tail.  A row with any
  *       status bit set is inert: all -1 and out_len 0.
- * Status bits are ORed (EMPTY alone when L <= 0).
+ * Status bits are ORed (EMPTY or LONG alone when L is out of range).
  * --------------------------------------------------------------------------- */
 #define PAGE4_EMPTY 1
 #define PAGE4_PARTIAL 2
 #define PAGE4_TAIL 4
 #define PAGE4_PAGE 8
 #define PAGE4_OVERFLOW 16
+#define PAGE4_SEQ 32
+#define PAGE4_LONG 64
+#define PAGE4_MAX_LIVE (1 << 26)
 
 int oracle_qsa_page4_table(const int32_t* tokens, int64_t token_stride, int32_t n_tokens,
                            const int32_t* live_len, const int32_t* block_table,
-                           int32_t max_pages, const int32_t* row_seq, int32_t num_pages,
+                           int32_t max_pages, const int32_t* row_seq, int32_t n_seqs,
+                           int32_t num_pages,
                            int32_t page_size, int32_t vpages_per_page, int32_t rows,
                            int32_t* out_table, int32_t out_stride, int32_t* out_len,
                            int32_t* out_status) {
   if (!tokens || !live_len || !block_table || !out_table || !out_len || !out_status ||
       rows < 0 || n_tokens < 0 || token_stride < n_tokens || max_pages < 1 ||
       page_size < 4 || page_size % 4 != 0 || vpages_per_page < page_size / 4 ||
-      out_stride < 1 || num_pages < 0)
+      out_stride < 1 || num_pages < 0 || n_seqs < 1)
     return ORACLE_ERR_ARG;
   int failed = 0;
 #pragma omp parallel for schedule(dynamic, 16)
@@ -339,8 +344,8 @@ int oracle_qsa_page4_table(const int32_t* tokens, int64_t token_stride, int32_t 
     for (int32_t i = 0; i < out_stride; ++i) orow[i] = -1;
     out_len[r] = 0;
     const int32_t L = live_len[r];
-    if (L <= 0) {
-      out_status[r] = PAGE4_EMPTY;
+    if (L <= 0 || L > PAGE4_MAX_LIVE) {
+      out_status[r] = L <= 0 ? PAGE4_EMPTY : PAGE4_LONG;
       continue;
     }
     /* S: the live selected positions, sorted, duplicates removed. */
@@ -365,8 +370,9 @@ int oracle_qsa_page4_table(const int32_t* tokens, int64_t token_stride, int32_t 
 
     const int32_t c = (L - 1) / 4;
     const int32_t seq = row_seq ? row_seq[r] : 0;
-    const int32_t* btab = block_table + (int64_t)seq * max_pages;
-    int status = 0, n_full = 0, below = 0, n_tail = 0;
+    const int seq_ok = seq >= 0 && seq < n_seqs;
+    const int32_t* btab = block_table + (int64_t)(seq_ok ? seq : 0) * max_pages;
+    int status = seq_ok ? 0 : PAGE4_SEQ, n_full = 0, below = 0, n_tail = 0;
     /* Walk S in order: whole blocks below c become pages. */
     int32_t i = 0;
     while (i < m && set[i] < 4 * c) {
@@ -384,7 +390,7 @@ int oracle_qsa_page4_table(const int32_t* tokens, int64_t token_stride, int32_t 
     if (n_pages > out_stride) status |= PAGE4_OVERFLOW;
     if (n_tail > 0) ids[n_full] = c;
     /* Logical block -> virtual page-4 id through the physical block table. */
-    for (int32_t k = 0; k < n_pages; ++k) {
+    for (int32_t k = 0; seq_ok && k < n_pages; ++k) {
       const int32_t b = ids[k];
       const int64_t lp = (int64_t)b * 4 / page_size;
       const int32_t p = lp < max_pages ? btab[lp] : -1;

@@ -26,6 +26,9 @@ PAGE4_PARTIAL = 2
 PAGE4_TAIL = 4
 PAGE4_PAGE = 8
 PAGE4_OVERFLOW = 16
+PAGE4_SEQ = 32
+PAGE4_LONG = 64
+PAGE4_MAX_LIVE = 1 << 26
 
 
 class OracleError(RuntimeError):
@@ -86,7 +89,8 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.oracle_qsa_page4_table.argtypes = [
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_void_p]
     _lib_cache[path] = lib
     return lib
 
@@ -199,14 +203,13 @@ def qsa_page4_table(tokens: np.ndarray, live_len, block_table: np.ndarray, *, nu
     seq = None if row_seq is None else np.ascontiguousarray(row_seq, dtype=np.int32)
     if live.shape != (rows,) or (seq is not None and seq.shape != (rows,)):
         raise ValueError("live_len and row_seq must be [rows]")
-    if seq is not None and rows and (seq.min() < 0 or seq.max() >= bt.shape[0]):
-        raise ValueError("row_seq names a sequence outside block_table")
     table = np.empty((rows, out_stride), dtype=np.int32)
     lens = np.empty(rows, dtype=np.int32)
     status = np.empty(rows, dtype=np.int32)
     rc = load(lib_path).oracle_qsa_page4_table(
         tokens.ctypes.data, n_tok, n_tok, live.ctypes.data, bt.ctypes.data, bt.shape[1],
-        None if seq is None else seq.ctypes.data, num_pages, page_size, vpages_per_page, rows,
+        None if seq is None else seq.ctypes.data, bt.shape[0], num_pages, page_size,
+        vpages_per_page, rows,
         table.ctypes.data, out_stride, lens.ctypes.data, status.ctypes.data)
     if rc != 0:
         raise OracleError(rc)

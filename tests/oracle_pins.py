@@ -465,7 +465,211 @@ def pin_topk_errors(lib: str) -> None:
         assert c.oracle_topk_select(*bad) == oracle.ORACLE_ERR_ARG, bad[1:6]
 
 
+
+# ------------------------------------------------- virtual page-4 tables
+def _page4_golden():
+    cases = []
+    with open(os.path.join(GOLDEN, "page4_table_examples.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            lhs, rhs = line.split("=>")
+            name, P, V, npg, stride, btab, L, toks = lhs.split()
+            table, ln, st = rhs.split()
+            ints = lambda t: [int(x) for x in t.split(",")]  # noqa: E731
+            cases.append(dict(name=name, P=int(P), V=int(V), num_pages=int(npg),
+                              out_stride=int(stride), btab=ints(btab), L=int(L),
+                              tokens=ints(toks), table=ints(table), len=int(ln),
+                              status=int(st)))
+    return cases
+
+
+def pin_page4_golden(lib: str) -> None:
+    """The hand-worked examples of tests/golden/page4_table_examples.txt."""
+    cases = _page4_golden()
+    assert len(cases) >= 12
+    for c in cases:
+        t, ln, st = oracle.qsa_page4_table(
+            np.array([c["tokens"]], np.int32), [c["L"]], np.array([c["btab"]], np.int32),
+            num_pages=c["num_pages"], page_size=c["P"], vpages_per_page=c["V"],
+            out_stride=c["out_stride"], lib_path=lib)
+        assert t[0].tolist() == c["table"] and ln[0] == c["len"] and st[0] == c["status"], (
+            c["name"], t[0].tolist(), int(ln[0]), int(st[0]))
+
+
+def _page4_brute(tokens, L, btab, num_pages, P, V, out_stride):
+    """The definition by enumeration over blocks (tiny inputs only): which of
+    blocks 0 .. c are fully, partly or not selected, then the view ids."""
+    if L <= 0:
+        return [-1] * out_stride, 0, 1
+    if L > (1 << 26):
+        return [-1] * out_stride, 0, 64
+    S = {t for t in tokens if 0 <= t < L}
+    c = (L - 1) // 4
+    status, full = 0, []
+    for b in range(c):
+        n = sum((4 * b + i) in S for i in range(4))
+        if n == 4:
+            full.append(b)
+        elif n:
+            status |= 2
+    tail = [4 * c + i for i in range(4) if (4 * c + i) in S]
+    if tail and tail != list(range(4 * c, 4 * c + len(tail))):
+        status |= 4
+    pages = full + ([c] if tail else [])
+    if len(pages) > out_stride:
+        status |= 16
+    ids = []
+    for b in pages:
+        lp = 4 * b // P
+        p = btab[lp] if lp < len(btab) else -1
+        if not 0 <= p < num_pages:
+            status |= 8
+        ids.append(p * V + (4 * b % P) // 4)
+    if status:
+        return [-1] * out_stride, 0, status
+    ids = sorted(ids[:len(full)]) + ids[len(full):]
+    return ids + [-1] * (out_stride - len(ids)), 4 * len(full) + len(tail), 0
+
+
+def pin_page4_brute_force(lib: str) -> None:
+    """Random small rows with every kind of defect against the enumeration."""
+    rng = np.random.default_rng(17)
+    for trial in range(400):
+        P = int(rng.choice([4, 8, 16]))
+        V = P // 4 * int(rng.choice([1, 2]))
+        n_lp = int(rng.integers(1, 7))
+        num_pages = n_lp + int(rng.integers(0, 3))
+        btab = rng.permutation(num_pages)[:n_lp].astype(np.int32)
+        if trial % 7 == 0:
+            btab[rng.integers(0, n_lp)] = int(rng.choice([-1, num_pages, num_pages + 5]))
+        L = int(rng.integers(-2, P * n_lp + 6))
+        toks = []
+        for b in range(max(0, (L + 3) // 4)):
+            u = rng.random()
+            if u < 0.35:
+                toks += [4 * b + i for i in range(4)]
+            elif u < 0.40:
+                toks += [4 * b + i for i in range(4) if rng.random() < 0.7]
+        toks += [int(x) for x in rng.integers(-3, L + 8, size=int(rng.integers(0, 3)))]
+        toks = [int(x) for x in rng.permutation(np.array(toks, dtype=np.int64))]
+        if not toks:
+            toks = [-1]
+        stride = int(rng.integers(1, 12))
+        t, ln, st = oracle.qsa_page4_table(np.array([toks], np.int32), [L],
+                                           np.array([btab], np.int32), num_pages=num_pages,
+                                           page_size=P, vpages_per_page=V, out_stride=stride,
+                                           lib_path=lib)
+        want = _page4_brute(toks, L, btab.tolist(), num_pages, P, V, stride)
+        assert (t[0].tolist(), int(ln[0]), int(st[0])) == want, (trial, toks, L, btab, want)
+
+
+def _sequence_kv(kv: inputs.PagedCase, btab: np.ndarray):
+    """K, V (float64 [tokens][Hkv][D]) of the sequence whose logical page i is
+    physical page btab[i], read element by element through the pool strides."""
+    P, hkv, d = kv.page_size, kv.num_kv_heads, kv.head_dim
+    n = btab.size * P
+    t = np.arange(n)
+    base = (btab[t // P].astype(np.int64) * kv.page_stride + (t % P) * kv.token_stride)
+    idx = (base[:, None, None] + np.arange(hkv)[None, :, None] * kv.head_stride
+           + np.arange(d)[None, None, :])
+    ks = kv.k_store.reshape(-1)[kv.k_offset + idx]
+    vs = kv.v_store.reshape(-1)[kv.v_offset + idx]
+    return decode_kv(ks, kv.kv_dtype, kv.k_scale), decode_kv(vs, kv.kv_dtype, kv.v_scale)
+
+
+def pin_page4_attention(lib: str) -> None:
+    """End to end: paged attention through the built page-4 view equals dense
+    attention (torch, float64) over exactly the selected token positions, for
+    interleaved and contiguous pools, tails 0-3 and every token order."""
+    for layout, tail, order in (("interleaved", 3, "shuffled"), ("contiguous", 1, "blocks"),
+                                ("interleaved", 0, "expanded"), ("contiguous", 2, "shuffled")):
+        case = inputs.page4_selection_case(rows=5, selected_blocks=6, tail=tail, seq_blocks=32,
+                                           page_size=8, order=order, layout=layout, seed=3,
+                                           with_kv=True, head_dim=32, num_q_heads=2)
+        t, ln, st = oracle.qsa_page4_table(case.tokens, case.live_len, case.block_table,
+                                           **case.builder_kwargs(), lib_path=lib)
+        assert np.all(st == 0) and np.all(ln == 4 * 6 + tail)
+        got = run(inputs.page4_view(case.kv, t, ln), lib)
+        kv = case.kv
+        K, V = _sequence_kv(kv, case.block_table[0])     # logical token order
+        for r in range(case.rows):
+            sel = sorted({int(x) for x in case.tokens[r] if 0 <= x < case.live_len[r]})
+            want = sdpa(kv.q[r], K[sel], V[sel], kv.sm_scale)
+            close(got[r], want, rtol=1e-10, atol=1e-12, what=(layout, tail, order, r))
+
+
+def pin_page4_invariants(lib: str) -> None:
+    case = inputs.page4_selection_case(rows=64, selected_blocks=20, tail=2, seq_blocks=256,
+                                       page_size=16, order="blocks", seed=8)
+    kw = case.builder_kwargs()
+    t0, l0, s0 = oracle.qsa_page4_table(case.tokens, case.live_len, case.block_table, **kw,
+                                        lib_path=lib)
+    assert np.all(s0 == 0)
+    rng = np.random.default_rng(2)
+    # Token order, duplicates, stale positions past the live length and
+    # padding do not matter.
+    noisy = []
+    for r in range(case.rows):
+        row = case.tokens[r]
+        extra = np.concatenate([row[rng.integers(0, row.size, 9)],
+                                case.live_len[r] + rng.integers(0, 50, 5), [-1, -7]])
+        noisy.append(rng.permutation(np.concatenate([row, extra])))
+    t1, l1, s1 = oracle.qsa_page4_table(np.array(noisy, np.int32), case.live_len,
+                                        case.block_table, **kw, lib_path=lib)
+    assert np.array_equal(t0, t1) and np.array_equal(l0, l1) and np.array_equal(s0, s1)
+    # Rows are independent.
+    for r in (0, 31, 63):
+        t2, l2, _ = oracle.qsa_page4_table(case.tokens[r:r + 1], case.live_len[r:r + 1],
+                                           case.block_table, **kw, lib_path=lib)
+        assert np.array_equal(t2[0], t0[r]) and l2[0] == l0[r]
+    # Renaming physical pages renames the ids and keeps the full part sorted.
+    perm = rng.permutation(case.num_pages).astype(np.int32)
+    t3, l3, _ = oracle.qsa_page4_table(case.tokens, case.live_len, perm[case.block_table],
+                                       **kw, lib_path=lib)
+    V = case.vpages_per_page
+    nf = (l0 - 2) // 4
+    for r in range(case.rows):
+        mapped = [perm[i // V] * V + i % V for i in t0[r, :nf[r] + 1]]
+        assert sorted(mapped[:-1]) == t3[r, :nf[r]].tolist() and mapped[-1] == t3[r, nf[r]]
+        assert np.all(np.diff(t3[r, :nf[r]]) >= 0) and np.all(t3[r, nf[r] + 1:] == -1)
+    # The rows of a second sequence use that sequence's table.
+    bt2 = np.stack([case.block_table[0], perm[case.block_table[0]]])
+    t4, _, _ = oracle.qsa_page4_table(case.tokens, case.live_len, bt2,
+                                      **{**kw, "row_seq": np.ones(case.rows, np.int32)},
+                                      lib_path=lib)
+    assert np.array_equal(t4, t3)
+    t5, _, s5 = oracle.qsa_page4_table(case.tokens, case.live_len, bt2,
+                                       **{**kw, "row_seq": np.full(case.rows, 2, np.int32)},
+                                       lib_path=lib)
+    assert np.all(s5 == oracle.PAGE4_SEQ) and np.all(t5 == -1)
+
+
+def pin_page4_errors(lib: str) -> None:
+    """Bad sizes are rejected before any row is looked at."""
+    c = oracle.load(lib)
+    tok = np.zeros((1, 4), np.int32)
+    live = np.ones(1, np.int32)
+    bt = np.zeros((1, 2), np.int32)
+    out = np.zeros(8, np.int32)
+    ln = np.zeros(1, np.int32)
+    st = np.zeros(1, np.int32)
+
+    def call(n_tok=4, stride=4, max_pages=2, n_seqs=1, num_pages=2, P=16, V=4, rows=1,
+             out_stride=4):
+        return c.oracle_qsa_page4_table(tok.ctypes.data, stride, n_tok, live.ctypes.data,
+                                        bt.ctypes.data, max_pages, None, n_seqs, num_pages, P,
+                                        V, rows, out.ctypes.data, out_stride, ln.ctypes.data,
+                                        st.ctypes.data)
+    assert call() == 0
+    for bad in (dict(n_tok=5), dict(rows=-1), dict(P=6), dict(P=0), dict(V=3), dict(max_pages=0),
+                dict(out_stride=0), dict(n_seqs=0), dict(num_pages=-1)):
+        assert call(**bad) == oracle.ORACLE_ERR_ARG, bad
+
+
 ALL_PINS = [pin_e4m3_vs_torch, pin_e4m3_golden, pin_f16_vs_numpy, pin_sdpa,
             pin_sparse_vs_masked_sdpa, pin_closed_forms, pin_invariants, pin_errors,
             pin_topk_vs_stable_sort, pin_topk_brute_force, pin_topk_total_order,
-            pin_topk_closed_forms, pin_topk_invariants, pin_topk_errors]
+            pin_topk_closed_forms, pin_topk_invariants, pin_topk_errors,
+            pin_page4_golden, pin_page4_brute_force, pin_page4_attention,
+            pin_page4_invariants, pin_page4_errors]
