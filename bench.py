@@ -143,6 +143,86 @@ def bench_topk(args) -> int:
     return 0
 
 
+def page4_alg_bytes(case) -> int:
+    """Bytes one builder call must move: every row's selection entries and
+    live length read, one block-table entry read per output page, the whole
+    output row plus its length and status written."""
+    rows = case.rows
+    n_pages = case.meta["selected_blocks"] + (1 if case.meta["tail"] else 0)
+    return rows * (case.n_tokens * 4 + 4 + n_pages * 4 + case.out_stride * 4 + 8)
+
+
+def cpu_baseline_page4(case, budget_s: float) -> dict:
+    """The oracle's table builder, as it is, on a bounded sample of rows (the
+    first rows of the workload, doubling until about `budget_s`)."""
+    import oracle
+
+    rows, el = 64, 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.qsa_page4_table(case.tokens[:rows], case.live_len[:rows], case.block_table,
+                               **case.builder_kwargs())
+        el = time.perf_counter() - t0
+        if el >= budget_s / 3 or rows >= case.rows:
+            break
+        rows = min(case.rows, rows * 2)
+    gbs = page4_alg_bytes(case) * rows / case.rows / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {rows} of {case.rows} rows, {el * 1e3:.1f} ms"}
+
+
+def bench_page4(args) -> int:
+    """Virtual page-4 table building: one step = one qsa_build_page4_table
+    call over every row.  `value` is the call's algorithmic bytes (selections
+    read, block-table entries looked up, tables written) per average call
+    time; the call is one kernel."""
+    import torch
+
+    from fp8_kv_amd import inputs, pgqa
+
+    pgqa.load()
+    torch.cuda.set_device(0)
+    case = inputs.page4_workload_case(args.workload)
+    R = max(1, args.pools)
+    toks = [torch.from_numpy(case.tokens).to("cuda")]
+    for _ in range(R - 1):
+        toks.append(toks[0].clone())
+    live = torch.from_numpy(case.live_len).to("cuda")
+    bt = torch.from_numpy(case.block_table).to("cuda")
+    out_t = torch.empty((case.rows, case.out_stride), dtype=torch.int32, device="cuda")
+    out_l = torch.empty(case.rows, dtype=torch.int32, device="cuda")
+    out_s = torch.empty(case.rows, dtype=torch.int32, device="cuda")
+    kw = case.builder_kwargs()
+    kw.pop("row_seq")
+
+    def call(i):
+        pgqa.qsa_build_page4_table(toks[i % R], live, bt, out_table=out_t, out_len=out_l,
+                                   out_status=out_s, **kw)
+
+    ms = time_steps(call, args.steps, args.warmup, R, not args.eager)
+    alg = page4_alg_bytes(case)
+    gbs = alg / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "HBM GB/s and µs/call, virtual page-4 table build from QSA selections",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": args.workload, "rows": case.rows, "tokens_per_row": case.n_tokens,
+                   "page_size": case.page_size, "vpages_per_page": case.vpages_per_page,
+                   "out_stride": case.out_stride, "selections_rotated": R,
+                   "us_per_call": round(ms * 1e3, 3), "alg_bytes_per_call": alg,
+                   "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "page4_kernel", "kernel_us": round(ms * 1e3, 3)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_page4(case, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def time_steps(step, steps: int, warmup: int, R: int, use_graph: bool) -> float:
     """Average milliseconds per step over exactly `steps` steps, timed with HIP
     events on the stream the kernels run on.  With use_graph the R steps of
@@ -207,6 +287,8 @@ def main() -> int:
 
     if args.workload in inputs.TOPK_WORKLOADS:
         return bench_topk(args)
+    if args.workload in inputs.PAGE4_WORKLOADS:
+        return bench_page4(args)
 
     import torch
 

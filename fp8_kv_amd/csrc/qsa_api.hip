@@ -4,6 +4,7 @@
 // any HIP call: an argument error launches nothing and writes nothing.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdint>
 
 #include "pgqa.h"
@@ -27,11 +28,8 @@ int qsa_topk_select(const float* scores, int64_t row_stride, const int32_t* n_va
   if (rows == 0) return PGQA_OK;
   if (!scores || (k > 0 && !out_idx)) return PGQA_ERR_NULL;
   if (row_stride < n_blocks || row_stride < 0) return PGQA_ERR_LAYOUT;
-  const auto misaligned4 = [](const void* ptr) {
-    return (reinterpret_cast<uintptr_t>(ptr) & 3u) != 0;
-  };
-  if (misaligned4(scores) || misaligned4(out_idx) || misaligned4(n_valid) ||
-      misaligned4(out_count))
+  if (!aligned(scores, 4) || !aligned(out_idx, 4) || !aligned(n_valid, 4) ||
+      !aligned(out_count, 4))
     return PGQA_ERR_LAYOUT;
   qsa::TopkParams p;
   p.scores = scores;
@@ -45,6 +43,53 @@ int qsa_topk_select(const float* scores, int64_t row_stride, const int32_t* n_va
   const bool vec = aligned(scores, 16) && row_stride % 4 == 0 && n_blocks % 4 == 0;
   if (qsa::launch_topk(p, vec, static_cast<hipStream_t>(stream)) != hipSuccess)
     return PGQA_ERR_HIP;
+  return PGQA_OK;
+}
+
+int qsa_build_page4_table(const int32_t* tokens, int64_t token_stride, int32_t n_tokens,
+                          const int32_t* live_len, const int32_t* block_table,
+                          int32_t max_pages, const int32_t* row_seq, int32_t n_seqs,
+                          int32_t num_pages, int32_t page_size, int32_t vpages_per_page,
+                          int32_t rows, int32_t* out_table, int32_t out_stride,
+                          int32_t* out_len, int32_t* out_status, void* stream) {
+  static_assert(PGQA_QSA_MAX_SEL_TOKENS == qsa::kPage4MaxTokens, "token limit mismatch");
+  static_assert(PGQA_PAGE4_EMPTY == qsa::kPage4Empty && PGQA_PAGE4_PARTIAL == qsa::kPage4Partial &&
+                    PGQA_PAGE4_TAIL == qsa::kPage4Tail && PGQA_PAGE4_PAGE == qsa::kPage4Page &&
+                    PGQA_PAGE4_OVERFLOW == qsa::kPage4Overflow &&
+                    PGQA_PAGE4_SEQ == qsa::kPage4Seq && PGQA_PAGE4_LONG == qsa::kPage4Long &&
+                    PGQA_PAGE4_MAX_LIVE == qsa::kPage4MaxLive,
+                "status codes mismatch");
+  if (rows < 0 || n_tokens < 0 || n_tokens > PGQA_QSA_MAX_SEL_TOKENS || max_pages < 1 ||
+      n_seqs < 1 || num_pages < 0 || page_size < 4 || page_size % 4 != 0 || out_stride < 1 ||
+      vpages_per_page < page_size / 4 ||
+      static_cast<int64_t>(num_pages) * vpages_per_page > INT32_MAX)
+    return PGQA_ERR_SHAPE;
+  if (rows == 0) return PGQA_OK;
+  if ((!tokens && n_tokens > 0) || !live_len || !block_table || !out_table || !out_len)
+    return PGQA_ERR_NULL;
+  if (token_stride < n_tokens) return PGQA_ERR_LAYOUT;
+  if (!aligned(tokens, 4) || !aligned(live_len, 4) || !aligned(block_table, 4) ||
+      !aligned(row_seq, 4) || !aligned(out_table, 4) || !aligned(out_len, 4) ||
+      !aligned(out_status, 4))
+    return PGQA_ERR_LAYOUT;
+  qsa::Page4Params p;
+  p.tokens = tokens;
+  p.token_stride = token_stride;
+  p.n_tokens = n_tokens;
+  p.live_len = live_len;
+  p.block_table = block_table;
+  p.max_pages = max_pages;
+  p.row_seq = row_seq;
+  p.n_seqs = n_seqs;
+  p.num_pages = num_pages;
+  p.page_size = page_size;
+  p.vpages_per_page = vpages_per_page;
+  p.rows = rows;
+  p.out_table = out_table;
+  p.out_stride = out_stride;
+  p.out_len = out_len;
+  p.out_status = out_status;
+  if (qsa::launch_page4(p, static_cast<hipStream_t>(stream)) != hipSuccess) return PGQA_ERR_HIP;
   return PGQA_OK;
 }
 

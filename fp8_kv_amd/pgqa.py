@@ -30,8 +30,14 @@ SIZE_MAX = ctypes.c_size_t(-1).value
 # Every symbol include/pgqa.h declares.
 EXPORTS = ("paged_gqa_workspace_bytes", "paged_gqa_num_splits", "paged_gqa_decode",
            "paged_gqa_prefill_sparse", "paged_gqa_decode_partial", "paged_gqa_merge_partials",
-           "e4m3_decode_table", "qsa_topk_select", "pgqa_error_string")
+           "e4m3_decode_table", "qsa_topk_select", "qsa_build_page4_table",
+           "pgqa_error_string")
 QSA_MAX_BLOCKS = 65536
+QSA_MAX_SEL_TOKENS = 8192
+# Row status bits of qsa_build_page4_table.
+PAGE4_EMPTY, PAGE4_PARTIAL, PAGE4_TAIL, PAGE4_PAGE = 1, 2, 4, 8
+PAGE4_OVERFLOW, PAGE4_SEQ, PAGE4_LONG = 16, 32, 64
+PAGE4_MAX_LIVE = 1 << 26
 
 
 class PgqaError(RuntimeError):
@@ -84,6 +90,9 @@ def _lib(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.e4m3_decode_table.argtypes = [vp, vp]
     lib.qsa_topk_select.restype = ctypes.c_int
     lib.qsa_topk_select.argtypes = [vp, ctypes.c_int64, vp, i32, i32, i32, vp, vp, vp]
+    lib.qsa_build_page4_table.restype = ctypes.c_int
+    lib.qsa_build_page4_table.argtypes = [vp, ctypes.c_int64, i32, vp, vp, i32, vp, i32, i32, i32,
+                                          i32, i32, vp, i32, vp, vp, vp]
     lib.pgqa_error_string.restype = ctypes.c_char_p
     lib.pgqa_error_string.argtypes = [ctypes.c_int]
     _LIB = lib
@@ -235,6 +244,40 @@ def qsa_topk_select(scores, k: int, n_valid=None, n_blocks: int | None = None, o
                                 _stream_handle(stream))
     _check(rc, "qsa_topk_select")
     return out_idx, out_count
+
+
+def qsa_build_page4_table(tokens, live_len, block_table, *, num_pages: int, page_size: int,
+                          vpages_per_page: int, out_stride: int, row_seq=None, out_table=None,
+                          out_len=None, out_status=None, stream=None):
+    """Virtual page-4 table of each row's expanded QSA selection (see
+    include/pgqa.h).  tokens: int32 device tensor [rows][n] (row stride taken
+    from the tensor); live_len int32 [rows]; block_table int32
+    [n_seqs][max_pages]; row_seq int32 [rows] or None.  Returns (out_table
+    int32 [rows][out_stride], out_len int32 [rows], out_status int32 [rows]),
+    allocating them when not given."""
+    import torch
+
+    if tokens.dim() != 2 or tokens.dtype != torch.int32 or (tokens.shape[1] > 1 and
+                                                            tokens.stride(1) != 1):
+        raise ValueError("tokens must be an int32 [rows][n] tensor with unit column stride")
+    if block_table.dim() != 2 or block_table.dtype != torch.int32 or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 [n_seqs][max_pages] tensor")
+    rows, n = tokens.shape
+    dev = tokens.device
+    if out_table is None:
+        out_table = torch.empty((rows, out_stride), dtype=torch.int32, device=dev)
+    if out_len is None:
+        out_len = torch.empty(rows, dtype=torch.int32, device=dev)
+    if out_status is None:
+        out_status = torch.empty(rows, dtype=torch.int32, device=dev)
+    stride = tokens.stride(0) if rows > 1 and n > 0 else n
+    rc = _lib().qsa_build_page4_table(
+        _ptr(tokens), int(stride), int(n), _ptr(live_len), _ptr(block_table),
+        int(block_table.shape[1]), _ptr(row_seq), int(block_table.shape[0]), int(num_pages),
+        int(page_size), int(vpages_per_page), int(rows), _ptr(out_table), int(out_stride),
+        _ptr(out_len), _ptr(out_status), _stream_handle(stream))
+    _check(rc, "qsa_build_page4_table")
+    return out_table, out_len, out_status
 
 
 # ------------------------------------------------------------ device inputs

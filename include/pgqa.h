@@ -233,6 +233,74 @@ int qsa_topk_select(const float* scores, int64_t row_stride, const int32_t* n_va
                     int32_t rows, int32_t n_blocks, int32_t k, int32_t* out_idx,
                     int32_t* out_count, void* stream);
 
+/*
+ * Virtual page-4 table of expanded QSA selections (source: "[Kernel][SM70]
+ * Accelerate Qwen3.8 QSA paged prefill", Purpose and Changes -- each selected
+ * four-token block is exposed as a zero-copy page of a page-4 view of the KV
+ * pool, the pages are locality-sorted, the causal partial page is kept last
+ * and checked against the expanded selection, positions past the live length
+ * are clamped away and invalid requests are inert).  The result is what
+ * paged_gqa_prefill_sparse takes as row_tables / row_lens with page_size 4
+ * over the view: k_base and v_base unchanged, page_stride = 4 * token_stride,
+ * num_pages = num_pages * vpages_per_page.
+ *
+ * Per row r, with L = live_len[r] and c = (L - 1) / 4 (the 4-token block that
+ * holds the row's own position):
+ *   S     = the distinct positions t listed in row r with 0 <= t < L
+ *           (order, duplicates, padding < 0 and positions >= L do not matter);
+ *   pages = the blocks b < c with all of 4b .. 4b+3 in S; any other position
+ *           of S below 4c makes the row invalid (PARTIAL);
+ *   tail  = S ∩ [4c, L), which must be 4c .. 4c + n_tail - 1 (else TAIL);
+ *   id(b) = p * vpages_per_page + (4b mod page_size) / 4 where
+ *           p = block_table[seq][4b / page_size] must exist (4b / page_size <
+ *           max_pages) and lie in [0, num_pages) (else PAGE);
+ *   row   = the pages' ids ascending, then id(c) if n_tail > 0, then -1 up
+ *           to out_stride; out_len = 4 * |pages| + n_tail.
+ * A row with any status bit set is inert: all -1, out_len 0.
+ *
+ *   tokens          int32 [rows][token_stride] (device): the expanded
+ *                   selection, n_tokens entries per row, logical positions in
+ *                   the row's sequence, -1 (any negative) = padding.  May be
+ *                   NULL when n_tokens is 0.
+ *   n_tokens        0 .. PGQA_QSA_MAX_SEL_TOKENS.
+ *   live_len        int32 [rows] (device): tokens 0 .. L-1 exist for the row
+ *                   (its position + 1).  L <= 0: EMPTY; L above
+ *                   PGQA_PAGE4_MAX_LIVE: LONG (the row is inert).
+ *   block_table     int32 [n_seqs][max_pages] (device): physical page of each
+ *                   logical page of page_size tokens.
+ *   row_seq         int32 [rows] (device) or NULL (every row in sequence 0):
+ *                   a value outside [0, n_seqs) gives SEQ.
+ *   num_pages       physical pages of the pool (page ids are checked).
+ *   page_size       tokens per physical page, a multiple of 4.
+ *   vpages_per_page page-4 views per physical page: page_stride /
+ *                   (4 * token_stride) of the pool (page_size / 4 for separate
+ *                   K and V arrays, page_size / 2 for interleaved K/V pages);
+ *                   >= page_size / 4, num_pages * vpages_per_page <= INT32_MAX.
+ *   out_table       int32 [rows][out_stride] (device), every entry written.
+ *   out_len         int32 [rows] (device).
+ *   out_status      int32 [rows] (device) or NULL: OR of PGQA_PAGE4_* bits.
+ * Caller-owned device memory; nothing is allocated; runs on `stream`.
+ * Errors: PGQA_ERR_SHAPE (sizes out of range), PGQA_ERR_NULL (a required
+ * pointer missing while rows > 0), PGQA_ERR_LAYOUT (token_stride < n_tokens or
+ * a pointer not 4-byte aligned), PGQA_ERR_HIP (launch refused).  Values inside
+ * the device arrays are checked per row and reported in out_status.
+ */
+#define PGQA_QSA_MAX_SEL_TOKENS 8192
+#define PGQA_PAGE4_MAX_LIVE (1 << 26)
+#define PGQA_PAGE4_EMPTY 1      /* live_len <= 0 */
+#define PGQA_PAGE4_PARTIAL 2    /* a block below the causal one partly selected */
+#define PGQA_PAGE4_TAIL 4       /* causal-block positions not a prefix of it */
+#define PGQA_PAGE4_PAGE 8       /* a needed page missing from the table or out of range */
+#define PGQA_PAGE4_OVERFLOW 16  /* more pages than out_stride */
+#define PGQA_PAGE4_SEQ 32       /* row_seq outside [0, n_seqs) */
+#define PGQA_PAGE4_LONG 64      /* live_len above PGQA_PAGE4_MAX_LIVE */
+int qsa_build_page4_table(const int32_t* tokens, int64_t token_stride, int32_t n_tokens,
+                          const int32_t* live_len, const int32_t* block_table,
+                          int32_t max_pages, const int32_t* row_seq, int32_t n_seqs,
+                          int32_t num_pages, int32_t page_size, int32_t vpages_per_page,
+                          int32_t rows, int32_t* out_table, int32_t out_stride,
+                          int32_t* out_len, int32_t* out_status, void* stream);
+
 /* Static description of a return code. */
 const char* pgqa_error_string(int code);
 

@@ -1,6 +1,7 @@
 /*
- * oracle.c -- plain CPU oracle for paged grouped-query attention (fp64) and
- * for QSA top-k block selection (exact integer/ordering work).
+ * oracle.c -- plain CPU oracle for paged grouped-query attention (fp64), for
+ * QSA top-k block selection and for virtual page-4 tables of QSA selections
+ * (exact integer/ordering work).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
  * load this file; only the tests, the smoke check and the benchmark's CPU
@@ -32,6 +33,14 @@
  * reported in increasing index order.  Pinned by numpy's stable argsort,
  * brute-force rank counting, the IEEE totalOrder spot list
  * (tests/golden/fp32_total_order.txt), closed forms and invariants.
+ *
+ * The virtual page-4 table of a QSA selection ("[Kernel][SM70] Accelerate
+ * Qwen3.8 QSA paged prefill", Purpose and Changes) is integer work defined
+ * by set operations; the oracle writes them out (sort, dedupe, walk the
+ * blocks, look up pages, sort the ids).  Pinned by hand-worked examples
+ * (tests/golden/page4_table_examples.txt), enumeration over blocks on tiny
+ * inputs, invariants, and attention through the built table against dense
+ * attention over the selected positions.
  *
  * Every function here is pinned by the CPU test suite (closed forms,
  * invariants, and library routines: torch's float8_e4m3fn cast, numpy's

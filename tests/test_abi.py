@@ -192,3 +192,49 @@ def test_topk_limit_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define PGQA_QSA_MAX_BLOCKS (\d+)", text)
     assert m and int(m.group(1)) == pgqa.QSA_MAX_BLOCKS
+
+
+def test_page4_validation(lib):
+    """qsa_build_page4_table: every rejected call returns before any HIP call."""
+    f = lib.qsa_build_page4_table
+    ok = dict(tok=FAKE, stride=64, n=64, live=FAKE, bt=FAKE, mp=16, seq=None, ns=1, npg=16, P=16,
+              V=4, rows=2, out=FAKE, ostride=17, ln=FAKE, st=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["tok"], a["stride"], a["n"], a["live"], a["bt"], a["mp"], a["seq"], a["ns"],
+                 a["npg"], a["P"], a["V"], a["rows"], a["out"], a["ostride"], a["ln"], a["st"],
+                 None)
+
+    assert call(rows=0) == pgqa.PGQA_OK
+    for bad in (dict(rows=-1), dict(n=-1), dict(n=pgqa.QSA_MAX_SEL_TOKENS + 1,
+                                                 stride=pgqa.QSA_MAX_SEL_TOKENS + 1),
+                dict(mp=0), dict(ns=0), dict(npg=-1), dict(P=6), dict(P=0), dict(ostride=0),
+                dict(V=3), dict(npg=1 << 30, V=4)):
+        assert call(**bad) == pgqa.PGQA_ERR_SHAPE, bad
+    for name in ("tok", "live", "bt", "out", "ln"):
+        assert call(**{name: None}) == pgqa.PGQA_ERR_NULL, name
+    assert call(tok=None, n=0, rows=0) == pgqa.PGQA_OK
+    assert call(stride=63) == pgqa.PGQA_ERR_LAYOUT
+    for name in ("tok", "live", "bt", "seq", "out", "ln", "st"):
+        assert call(**{name: FAKE + 2}) == pgqa.PGQA_ERR_LAYOUT, name
+
+
+def test_page4_constants_match_header():
+    text = open(HEADER).read()
+    for name, val in (("PGQA_QSA_MAX_SEL_TOKENS", pgqa.QSA_MAX_SEL_TOKENS),
+                      ("PGQA_PAGE4_EMPTY", pgqa.PAGE4_EMPTY),
+                      ("PGQA_PAGE4_PARTIAL", pgqa.PAGE4_PARTIAL),
+                      ("PGQA_PAGE4_TAIL", pgqa.PAGE4_TAIL), ("PGQA_PAGE4_PAGE", pgqa.PAGE4_PAGE),
+                      ("PGQA_PAGE4_OVERFLOW", pgqa.PAGE4_OVERFLOW),
+                      ("PGQA_PAGE4_SEQ", pgqa.PAGE4_SEQ), ("PGQA_PAGE4_LONG", pgqa.PAGE4_LONG)):
+        m = re.search(rf"#define {name} (\d+)", text)
+        assert m and int(m.group(1)) == val, name
+    m = re.search(r"#define PGQA_PAGE4_MAX_LIVE \(1 << (\d+)\)", text)
+    assert m and (1 << int(m.group(1))) == pgqa.PAGE4_MAX_LIVE
+    import oracle
+    # The oracle uses the same bit values (it shares no code with the library).
+    assert (oracle.PAGE4_EMPTY, oracle.PAGE4_PARTIAL, oracle.PAGE4_TAIL, oracle.PAGE4_PAGE,
+            oracle.PAGE4_OVERFLOW, oracle.PAGE4_SEQ, oracle.PAGE4_LONG) == \
+        (pgqa.PAGE4_EMPTY, pgqa.PAGE4_PARTIAL, pgqa.PAGE4_TAIL, pgqa.PAGE4_PAGE,
+         pgqa.PAGE4_OVERFLOW, pgqa.PAGE4_SEQ, pgqa.PAGE4_LONG)

@@ -53,6 +53,24 @@ MUTANTS = {
     "topk_one_short": ("int32_t t = m < k ? m : k;", "int32_t t = m < k ? m : k - 1;"),
     "topk_rank_order_out": ("qsort(o, (size_t)t, sizeof(int32_t), cmp_int);", ";"),
     "topk_no_clamp": ("if (m > n_blocks) m = n_blocks;", ";"),
+    "page4_unsorted": ("qsort(ids, (size_t)n_full, sizeof(int32_t), cmp_int); /* locality order */",
+                       ";"),
+    "page4_sort_tail_too": ("qsort(ids, (size_t)n_full, sizeof(int32_t), cmp_int); /* locality",
+                            "qsort(ids, (size_t)n_pages, sizeof(int32_t), cmp_int); /* locality"),
+    "page4_views_ignored": ("ids[k] = p * vpages_per_page + (int32_t)",
+                            "ids[k] = p * (page_size / 4) + (int32_t)"),
+    "page4_group_index": ("(((int64_t)b * 4 % page_size) / 4)", "(((int64_t)b % page_size) / 4)"),
+    "page4_tail_len": ("out_len[r] = 4 * n_full + n_tail;", "out_len[r] = 4 * n_full;"),
+    "page4_causal_block": ("const int32_t c = (L - 1) / 4;", "const int32_t c = L / 4;"),
+    "page4_partial_ok": ("if (below != 4 * n_full) status |= PAGE4_PARTIAL;", ";"),
+    "page4_stale_kept": ("if (trow[i] >= 0 && trow[i] < L) set[m++] = trow[i];",
+                         "if (trow[i] >= 0 && trow[i] <= L) set[m++] = trow[i];"),
+    "page4_no_dedupe": ("if (u == 0 || set[i] != set[u - 1]) set[u++] = set[i];",
+                        "set[u++] = set[i];"),
+    "page4_tail_unchecked": ("if (n_tail > 0 && set[m - 1] != 4 * c + n_tail - 1) status |= PAGE4_TAIL;",
+                             ";"),
+    "page4_page_unchecked": ("if (p < 0 || p >= num_pages) {", "if (p < 0) {"),
+    "page4_overflow_unchecked": ("if (n_pages > out_stride) status |= PAGE4_OVERFLOW;", ";"),
 }
 
 
