@@ -16,7 +16,8 @@
 //   output = the pages' ids ascending, then id(c) if n_tail > 0, then -1;
 //            length 4 * pages + n_tail.  Invalid rows: all -1, length 0.
 //
-// One wave (64 lanes) owns one row; nothing needs a workgroup barrier.
+// One wave (64 lanes) owns one row; a workgroup of four waves shares the
+// hash set of the general path, which its waves use one at a time.
 //   1. Collection of the full blocks and the causal positions, two ways:
 //      - Expanded layout (no atomics): the row read as chunks of four entries
 //        from its start; a chunk 4b, 4b+1, 4b+2, 4b+3 with b < c is that
@@ -346,127 +347,164 @@ __device__ __forceinline__ bool has_adjacent_equal(const int32_t (&x)[E], int32_
   return __ballot(eq) != 0;
 }
 
+// Result of building one row's table (ids hold the row: full pages, then
+// the causal page).
+struct RowState {
+  int32_t status, n_full, n_tail;
+  bool retry;  // the expanded-layout attempt could not settle the row
+};
+
+// One attempt at a row with live length L (1 <= L <= kPage4MaxLive): the
+// expanded-layout collection when !general (which may ask for a retry), else
+// the general one through the hash set.
 template <int E>
-__global__ __launch_bounds__(64) void page4_kernel(Page4Params p, int32_t hash_log2) {
-  extern __shared__ uint32_t lds[];
-  const uint32_t hmask = (1u << hash_log2) - 1u;
-  uint32_t* slots = lds;                                       // [hmask + 1]
-  int32_t* ids = reinterpret_cast<int32_t*>(lds + hmask + 1);  // [64 E + 1]
-  const int row = blockIdx.x;
-  const int lane = threadIdx.x;
-  int32_t* orow = p.out_table + static_cast<int64_t>(row) * p.out_stride;
-  const int32_t L = p.live_len[row];
-
+__device__ __forceinline__ RowState attempt(const Page4Params& p, int row, int32_t L, bool general,
+                                            uint32_t* slots, uint32_t hmask, int32_t hash_log2,
+                                            int32_t* ids) {
+  const int lane = threadIdx.x & 63;
+  const int32_t c = (L - 1) >> 2;
+  const int32_t* trow = p.tokens + static_cast<int64_t>(row) * p.token_stride;
   int32_t status = 0;
-  if (L <= 0) status = kPage4Empty;
-  if (L > kPage4MaxLive) status = kPage4Long;
-  int32_t n_full = 0, n_tail = 0;
-  if (status == 0) {
-    const int32_t c = (L - 1) >> 2;
-    const int32_t* trow = p.tokens + static_cast<int64_t>(row) * p.token_stride;
-    // Pass 0 takes the expanded-layout path when the row allows it; pass 1
-    // (the general path) runs when it does not, or when the sorted ids show a
-    // block the fast path may have listed twice.
-    for (int pass = 0; pass < 2; ++pass) {
-      status = 0;
-      // ---- 1. the full blocks and the causal positions
-      Collected col;
-      const bool fast = pass == 0 && collect_fast(p, trow, L, c, ids, col);
-      if (!fast) col = collect_hash(p, trow, L, c, slots, hmask, hash_log2, ids);
-      n_full = col.n_full;
-      const uint32_t tmask = wave_or(col.tmask);
-      n_tail = __popc(tmask);
-      if (n_tail > 0 && tmask != (1u << n_tail) - 1u) status |= kPage4Tail;
-      if (__ballot(col.lost)) status |= kPage4Overflow;
-      if (col.n_claimed != n_full) status |= kPage4Partial;
-      const int32_t n_pages = n_full + (n_tail > 0 ? 1 : 0);
-      if (n_pages > p.out_stride) status |= kPage4Overflow;
-      if (n_tail > 0 && lane == 0) ids[n_full] = c;
-      lds_fence_wave();
 
-      // ---- 2. block -> view id through the sequence's block table; the
-      // table entries of a batch of 16 ids per lane are loaded together.
-      const int32_t seq = p.row_seq ? p.row_seq[row] : 0;
-      if (seq < 0 || seq >= p.n_seqs) {
-        status |= kPage4Seq;
-      } else {
-        const int32_t* btab = p.block_table + static_cast<int64_t>(seq) * p.max_pages;
-        const int32_t quarter = p.page_size >> 2;  // 4-token groups per physical page
-        const bool pow2 = (quarter & (quarter - 1)) == 0;
-        const int32_t qshift = __ffs(quarter) - 1;
-        bool bad = false;
-        constexpr int kLook = 16;
-        for (int32_t j0 = 0; j0 < n_pages; j0 += 64 * kLook) {
-          int32_t b[kLook], lp[kLook], pg[kLook];
-#pragma unroll
-          for (int u = 0; u < kLook; ++u) {
-            const int32_t j = j0 + 64 * u + lane;
-            b[u] = j < n_pages ? ids[j] : 0;
-            lp[u] = pow2 ? (b[u] >> qshift) : b[u] / quarter;
-          }
-#pragma unroll
-          for (int u = 0; u < kLook; ++u) {
-            const int32_t j = j0 + 64 * u + lane;
-            pg[u] = j < n_pages && lp[u] < p.max_pages ? btab[lp[u]] : -1;
-          }
-#pragma unroll
-          for (int u = 0; u < kLook; ++u) {
-            const int32_t j = j0 + 64 * u + lane;
-            if (j < n_pages) {
-              const bool ok = pg[u] >= 0 && pg[u] < p.num_pages;
-              bad |= !ok;
-              ids[j] = ok ? pg[u] * p.vpages_per_page + (b[u] - lp[u] * quarter) : -1;
-            }
-          }
-        }
-        if (__ballot(bad)) status |= kPage4Page;
-      }
-      lds_fence_wave();
+  // ---- 1. the full blocks and the causal positions
+  Collected col;
+  if (general)
+    col = collect_hash(p, trow, L, c, slots, hmask, hash_log2, ids);
+  else if (!collect_fast(p, trow, L, c, ids, col))
+    return RowState{0, 0, 0, true};
+  const int32_t n_full = col.n_full;
+  const uint32_t tmask = wave_or(col.tmask);
+  const int32_t n_tail = __popc(tmask);
+  if (n_tail > 0 && tmask != (1u << n_tail) - 1u) status |= kPage4Tail;
+  if (__ballot(col.lost)) status |= kPage4Overflow;
+  if (col.n_claimed != n_full) status |= kPage4Partial;
+  const int32_t n_pages = n_full + (n_tail > 0 ? 1 : 0);
+  if (n_pages > p.out_stride) status |= kPage4Overflow;
+  if (n_tail > 0 && lane == 0) ids[n_full] = c;
+  lds_fence_wave();
 
-      // ---- 3. locality order of the full pages
-      if (status == 0 && n_full > 1) {
-        int32_t x[E];
+  // ---- 2. block -> view id through the sequence's block table; the table
+  // entries of a batch of 16 ids per lane are loaded together.
+  const int32_t seq = p.row_seq ? p.row_seq[row] : 0;
+  if (seq < 0 || seq >= p.n_seqs) {
+    status |= kPage4Seq;
+  } else {
+    const int32_t* btab = p.block_table + static_cast<int64_t>(seq) * p.max_pages;
+    const int32_t quarter = p.page_size >> 2;  // 4-token groups per physical page
+    const bool pow2 = (quarter & (quarter - 1)) == 0;
+    const int32_t qshift = __ffs(quarter) - 1;
+    bool bad = false;
+    constexpr int kLook = 16;
+    for (int32_t j0 = 0; j0 < n_pages; j0 += 64 * kLook) {
+      int32_t b[kLook], lp[kLook], pg[kLook];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int32_t i = lane * E + e;
-          x[e] = i < n_full ? ids[i] : INT32_MAX;
-        }
-        wave_sort<E>(x);
-        if (fast && has_adjacent_equal<E>(x, n_full)) continue;  // recheck on the general path
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int32_t i = lane * E + e;
-          if (i < n_full) ids[i] = x[e];
-        }
-        lds_fence_wave();
+      for (int u = 0; u < kLook; ++u) {
+        const int32_t j = j0 + 64 * u + lane;
+        b[u] = j < n_pages ? ids[j] : 0;
+        lp[u] = pow2 ? (b[u] >> qshift) : b[u] / quarter;
       }
-      break;
+#pragma unroll
+      for (int u = 0; u < kLook; ++u) {
+        const int32_t j = j0 + 64 * u + lane;
+        pg[u] = j < n_pages && lp[u] < p.max_pages ? btab[lp[u]] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kLook; ++u) {
+        const int32_t j = j0 + 64 * u + lane;
+        if (j < n_pages) {
+          const bool ok = pg[u] >= 0 && pg[u] < p.num_pages;
+          bad |= !ok;
+          ids[j] = ok ? pg[u] * p.vpages_per_page + (b[u] - lp[u] * quarter) : -1;
+        }
+      }
     }
+    if (__ballot(bad)) status |= kPage4Page;
   }
+  lds_fence_wave();
+
+  // ---- 3. locality order of the full pages
+  if (status == 0 && n_full > 1) {
+    int32_t x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int32_t i = lane * E + e;
+      x[e] = i < n_full ? ids[i] : INT32_MAX;
+    }
+    wave_sort<E>(x);
+    // Two equal neighbours: the fast path may have listed a block twice.
+    if (!general && has_adjacent_equal<E>(x, n_full)) return RowState{0, 0, 0, true};
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int32_t i = lane * E + e;
+      if (i < n_full) ids[i] = x[e];
+    }
+    lds_fence_wave();
+  }
+  return RowState{status, n_full, n_tail, false};
+}
+
+// W waves, one row each; the hash set of the general path is shared by the
+// workgroup and used by one wave at a time (rows that need it are rare).
+template <int E, int W>
+__global__ __launch_bounds__(64 * W) void page4_kernel(Page4Params p, int32_t hash_log2) {
+  extern __shared__ uint32_t lds[];
+  constexpr int kIds = 64 * E + 4;  // per-wave id list (the causal page included)
+  const uint32_t hmask = (1u << hash_log2) - 1u;
+  uint32_t* slots = lds;            // [hmask + 1]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  int32_t* ids = reinterpret_cast<int32_t*>(lds + hmask + 1) + wave * kIds;
+  const int row = blockIdx.x * W + wave;
+  const bool active = row < p.rows;
+
+  RowState st{0, 0, 0, false};
+  int32_t L = 0;
+  if (active) {
+    L = p.live_len[row];
+    if (L <= 0)
+      st.status = kPage4Empty;
+    else if (L > kPage4MaxLive)
+      st.status = kPage4Long;
+    else
+      st = attempt<E>(p, row, L, false, slots, hmask, hash_log2, ids);
+  }
+  // The general path, one wave at a time (every wave reaches every barrier).
+  for (int w = 0; w < W; ++w) {
+    __syncthreads();
+    if (wave == w && active && st.retry)
+      st = attempt<E>(p, row, L, true, slots, hmask, hash_log2, ids);
+  }
+  if (!active) return;
 
   // ---- 4. the row: pages, causal page last, -1 padding; inert if invalid
-  const int32_t n_out = status == 0 ? n_full + (n_tail > 0 ? 1 : 0) : 0;
+  int32_t* orow = p.out_table + static_cast<int64_t>(row) * p.out_stride;
+  const int32_t n_out = st.status == 0 ? st.n_full + (st.n_tail > 0 ? 1 : 0) : 0;
   for (int32_t i = lane; i < p.out_stride; i += 64) orow[i] = i < n_out ? ids[i] : -1;
   if (lane == 0) {
-    p.out_len[row] = status == 0 ? 4 * n_full + n_tail : 0;
-    if (p.out_status) p.out_status[row] = status;
+    p.out_len[row] = st.status == 0 ? 4 * st.n_full + st.n_tail : 0;
+    if (p.out_status) p.out_status[row] = st.status;
   }
 }
 
+constexpr int kRowsPerGroup = 4;
+
 template <int E>
 hipError_t launch_e(const Page4Params& p, int32_t hash_log2, hipStream_t stream) {
-  const size_t lds = sizeof(uint32_t) * ((size_t{1} << hash_log2) + 64 * E + 1);
+  constexpr int W = kRowsPerGroup;
+  const auto bytes = [](size_t slots) {
+    return sizeof(uint32_t) * (slots + static_cast<size_t>(W) * (64 * E + 4));
+  };
+  const size_t lds = bytes(size_t{1} << hash_log2);
   if (lds > 65536) {
     // Beyond the default 64 KiB of dynamic LDS the limit must be raised
     // (once per process and instance; the largest size this instance uses).
     static const hipError_t raised = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(page4_kernel<E>),
-        hipFuncAttributeMaxDynamicSharedMemorySize,
-        static_cast<int>(sizeof(uint32_t) * (2 * kPage4MaxTokens + 64 * E + 1)));
+        reinterpret_cast<const void*>(page4_kernel<E, W>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes(2 * kPage4MaxTokens)));
     if (raised != hipSuccess) return raised;
   }
-  hipLaunchKernelGGL(page4_kernel<E>, dim3(static_cast<unsigned>(p.rows)), dim3(64), lds, stream,
-                     p, hash_log2);
+  const unsigned groups = static_cast<unsigned>((p.rows + W - 1) / W);
+  hipLaunchKernelGGL((page4_kernel<E, W>), dim3(groups), dim3(64 * W), lds, stream, p, hash_log2);
   return hipGetLastError();
 }
 
