@@ -515,3 +515,63 @@ def page4_workload_case(name: str, **overrides) -> Page4Case:
     kw = dict(PAGE4_WORKLOADS[name])
     kw.update(overrides)
     return page4_selection_case(**kw)
+
+
+@dataclass
+class SamplerCase:
+    """Sampler logits for combined top-k/top-p masking ("[Kernel][SM70] Scale
+    NVFP4 E4M3 decode batches", Purpose and Performance contract: B8/B16 x
+    248,320 logits, top-k 20, top-p 0.95)."""
+    logits: np.ndarray          # float32 [rows][V]
+    k: np.ndarray               # int32 [rows]
+    p: np.ndarray               # float32 [rows]
+    k_max: int
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def rows(self) -> int:
+        return int(self.logits.shape[0])
+
+    @property
+    def vocab(self) -> int:
+        return int(self.logits.shape[1])
+
+
+def sampler_case(*, rows: int, vocab: int, k=20, p=0.95, seed: int = 0, scale: float = 3.0,
+                 dist: str = "normal", k_max: int = 1024) -> SamplerCase:
+    """Seeded logits.  dist: "normal" (N(0, scale^2) fp32), "ties" (normal
+    rounded to multiples of 1/2, so many tokens share a logit), "flat" (every
+    logit 0), "peaked" (normal plus a few tokens raised by 10*scale).  k and p:
+    scalars or per-row sequences.  Seeds: SeedSequence(seed).spawn(2)
+    children draw the logits and the peaks, in that order."""
+    z_rng, x_rng = (np.random.default_rng(c) for c in np.random.SeedSequence(seed).spawn(2))
+    if dist in ("normal", "ties", "peaked"):
+        z = z_rng.standard_normal((rows, vocab), dtype=np.float32) * np.float32(scale)
+        if dist == "ties":
+            z = np.round(z * 2) / 2
+        if dist == "peaked":
+            for r in range(rows):
+                idx = x_rng.choice(vocab, size=min(5, vocab), replace=False)
+                z[r, idx] += np.float32(10 * scale)
+    elif dist == "flat":
+        z = np.zeros((rows, vocab), dtype=np.float32)
+    else:
+        raise ValueError(dist)
+    kk = np.ascontiguousarray(np.broadcast_to(np.asarray(k, dtype=np.int32), (rows,)))
+    pp = np.ascontiguousarray(np.broadcast_to(np.asarray(p, dtype=np.float32), (rows,)))
+    return SamplerCase(logits=np.ascontiguousarray(z.astype(np.float32)), k=kk, p=pp,
+                       k_max=k_max, meta=dict(seed=seed, dist=dist, scale=scale))
+
+
+# The pages' sampler workload: B8 and B16 rows of 248,320 logits with top-k 20
+# and top-p 0.95; logits ~ N(0, 3^2).
+SAMPLER_WORKLOADS = {
+    "sampler_topk_topp_b16_248320": dict(rows=16, vocab=248320, k=20, p=0.95, seed=91),
+    "sampler_topk_topp_b8_248320": dict(rows=8, vocab=248320, k=20, p=0.95, seed=92),
+}
+
+
+def sampler_workload_case(name: str, **overrides) -> SamplerCase:
+    kw = dict(SAMPLER_WORKLOADS[name])
+    kw.update(overrides)
+    return sampler_case(**kw)

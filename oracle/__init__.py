@@ -8,6 +8,8 @@ from .oracle import (  # noqa: F401
     ORACLE_ERR_ARG,
     ORACLE_ERR_PAGE,
     ORACLE_ERR_TABLE,
+    MASK_BAD_K,
+    MASK_BAD_P,
     PAGE4_EMPTY,
     PAGE4_LONG,
     PAGE4_MAX_LIVE,
@@ -25,5 +27,6 @@ from .oracle import (  # noqa: F401
     num_threads,
     paged_gqa,
     qsa_page4_table,
+    topk_topp_mask,
     topk_select,
 )

@@ -1,7 +1,8 @@
 /*
  * oracle.c -- plain CPU oracle for paged grouped-query attention (fp64), for
- * QSA top-k block selection and for virtual page-4 tables of QSA selections
- * (exact integer/ordering work).
+ * QSA top-k block selection, for virtual page-4 tables of QSA selections
+ * (exact integer/ordering work) and for combined top-k/top-p masking of
+ * sampler logits.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
  * load this file; only the tests, the smoke check and the benchmark's CPU
@@ -41,6 +42,13 @@
  * (tests/golden/page4_table_examples.txt), enumeration over blocks on tiny
  * inputs, invariants, and attention through the built table against dense
  * attention over the selected positions.
+ *
+ * Combined top-k / top-p masking of sampler logits ("[Kernel][SM70] Scale
+ * NVFP4 E4M3 decode batches", Purpose) is the sort order of the top-k
+ * selection followed by a cumulative-probability cut in fp64.  Pinned by
+ * hand-worked rows (tests/golden/topk_topp_examples.txt), a numpy float64
+ * formulation (lexsort, cumsum), closed forms (p = 1, k = 1, p = 0, flat
+ * rows) and invariants.
  *
  * Every function here is pinned by the CPU test suite (closed forms,
  * invariants, and library routines: torch's float8_e4m3fn cast, numpy's
@@ -418,6 +426,83 @@ int oracle_qsa_page4_table(const int32_t* tokens, int64_t token_stride, int32_t 
     }
     free(set);
     free(ids);
+  }
+  return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Combined top-k / top-p masking of sampler logits ("[Kernel][SM70] Scale
+ * NVFP4 E4M3 decode batches", Purpose: combined top-k/top-p masking for B8/B16
+ * x 248,320 logits; Performance contract: sampler top-k 20, top-p 0.95).
+ *
+ * Definition, per row r of V logits (k = k_row[r], p = p_row[r]):
+ *   k < 1 or k > k_max, or p NaN: the row is invalid (status bit 1 or 2)
+ *       and copied unchanged.
+ *   Order the V tokens by (logit descending, index ascending), logits ranked
+ *   by their IEEE 754 totalOrder keys.  The top-k set is the first
+ *   n = min(k, V) tokens of that order.
+ *   Top-p over them, in that order: with m the first logit, w_i = exp(z_i -
+ *   m) and W = sum of w_i, token i (1-based) stays iff i == 1 or
+ *   (w_1 + .. + w_{i-1}) / W < p.  p >= 1 keeps all n.
+ *   out[t] = logit[t] for kept tokens, -inf for every other token.
+ * Sums and exponentials in fp64.
+ * --------------------------------------------------------------------------- */
+#define MASK_BAD_K 1
+#define MASK_BAD_P 2
+
+int oracle_topk_topp_mask(const float* logits, int64_t row_stride, int32_t rows, int32_t V,
+                          const int32_t* k_row, const float* p_row, int32_t k_max,
+                          float* out, int64_t out_stride, int32_t* status, int32_t* n_kept) {
+  if (!logits || !k_row || !p_row || !out || !status || !n_kept || rows < 0 || V < 1 ||
+      row_stride < V || out_stride < V || k_max < 1)
+    return ORACLE_ERR_ARG;
+  int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t r = 0; r < rows; ++r) {
+    const float* z = logits + (int64_t)r * row_stride;
+    float* o = out + (int64_t)r * out_stride;
+    const int32_t k = k_row[r];
+    const float p = p_row[r];
+    int st = 0;
+    if (k < 1 || k > k_max) st |= MASK_BAD_K;
+    if (isnan(p)) st |= MASK_BAD_P;
+    status[r] = st;
+    if (st) {
+      for (int32_t t = 0; t < V; ++t) o[t] = z[t];
+      n_kept[r] = V;
+      continue;
+    }
+    keyed_t* items = (keyed_t*)malloc(sizeof(keyed_t) * (size_t)V);
+    if (!items) {
+#pragma omp atomic write
+      failed = 1;
+      continue;
+    }
+    for (int32_t t = 0; t < V; ++t) {
+      items[t].key = score_key(z[t]);
+      items[t].idx = t;
+    }
+    qsort(items, (size_t)V, sizeof(keyed_t), cmp_rank); /* logit desc, index asc */
+    const int32_t n = k < V ? k : V;
+    int32_t keep = n;
+    if (p < 1.0f) {
+      const double m = (double)z[items[0].idx];
+      double W = 0.0;
+      for (int32_t i = 0; i < n; ++i) W += exp((double)z[items[i].idx] - m);
+      double before = 0.0;
+      keep = 1;
+      for (int32_t i = 1; i < n; ++i) {
+        before += exp((double)z[items[i - 1].idx] - m);
+        if (before / W < (double)p)
+          keep = i + 1;
+        else
+          break;
+      }
+    }
+    for (int32_t t = 0; t < V; ++t) o[t] = -INFINITY;
+    for (int32_t i = 0; i < keep; ++i) o[items[i].idx] = z[items[i].idx];
+    n_kept[r] = keep;
+    free(items);
   }
   return failed ? ORACLE_ERR_NOMEM : ORACLE_OK;
 }

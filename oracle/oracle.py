@@ -30,6 +30,10 @@ PAGE4_SEQ = 32
 PAGE4_LONG = 64
 PAGE4_MAX_LIVE = 1 << 26
 
+# Row status bits of the top-k/top-p masking (see oracle.c).
+MASK_BAD_K = 1
+MASK_BAD_P = 2
+
 
 class OracleError(RuntimeError):
     def __init__(self, code: int):
@@ -90,6 +94,11 @@ def load(path: str = _LIB) -> ctypes.CDLL:
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_void_p]
+    lib.oracle_topk_topp_mask.restype = ctypes.c_int
+    lib.oracle_topk_topp_mask.argtypes = [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
         ctypes.c_void_p]
     _lib_cache[path] = lib
     return lib
@@ -214,3 +223,22 @@ def qsa_page4_table(tokens: np.ndarray, live_len, block_table: np.ndarray, *, nu
     if rc != 0:
         raise OracleError(rc)
     return table, lens, status
+
+
+def topk_topp_mask(logits: np.ndarray, k, p, *, k_max: int = 1024, lib_path: str = _LIB):
+    """Combined top-k/top-p masking of each row of fp32 logits [rows][V] (see
+    oracle.c).  k: int32 [rows]; p: float32 [rows].  Returns (out float32
+    [rows][V], status int32 [rows], n_kept int32 [rows])."""
+    z = np.ascontiguousarray(logits, dtype=np.float32)
+    rows, V = z.shape
+    kk = np.ascontiguousarray(np.broadcast_to(np.asarray(k, dtype=np.int32), (rows,)))
+    pp = np.ascontiguousarray(np.broadcast_to(np.asarray(p, dtype=np.float32), (rows,)))
+    out = np.empty_like(z)
+    status = np.empty(rows, dtype=np.int32)
+    kept = np.empty(rows, dtype=np.int32)
+    rc = load(lib_path).oracle_topk_topp_mask(z.ctypes.data, V, rows, V, kk.ctypes.data,
+                                              pp.ctypes.data, k_max, out.ctypes.data, V,
+                                              status.ctypes.data, kept.ctypes.data)
+    if rc != 0:
+        raise OracleError(rc)
+    return out, status, kept

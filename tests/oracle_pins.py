@@ -667,9 +667,145 @@ def pin_page4_errors(lib: str) -> None:
         assert call(**bad) == oracle.ORACLE_ERR_ARG, bad
 
 
+
+# ------------------------------------------------ top-k / top-p masking
+def _mask_golden():
+    cases = []
+    with open(os.path.join(GOLDEN, "topk_topp_examples.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            lhs, rhs = line.split("=>")
+            name, k, p, z = lhs.split()
+            logits = [math.log(float(v[2:])) for v in z.split(",")]
+            cases.append(dict(name=name, k=int(k), p=float(p), logits=logits,
+                              kept=[int(v) for v in rhs.split(",")]))
+    return cases
+
+
+def pin_mask_golden(lib: str) -> None:
+    cases = _mask_golden()
+    assert len(cases) >= 10
+    for c in cases:
+        z = np.array([c["logits"]], np.float32)
+        out, st, kept = oracle.topk_topp_mask(z, [c["k"]], [c["p"]], lib_path=lib)
+        got = np.flatnonzero(out[0] != -np.inf).tolist()
+        assert st[0] == 0 and got == c["kept"] and kept[0] == len(c["kept"]), (c["name"], got)
+        assert np.array_equal(out[0, got], z[0, got])
+
+
+def _mask_numpy(z: np.ndarray, k: int, p: float) -> np.ndarray:
+    """The definition with numpy: lexsort by (-logit, index), float64 softmax
+    over the first k, cumulative sums, the keep rule.  Returns kept indices."""
+    order = np.lexsort((np.arange(z.size), -z.astype(np.float64)))
+    top = order[:min(k, z.size)]
+    zt = z[top].astype(np.float64)
+    w = np.exp(zt - zt[0])
+    before = np.concatenate([[0.0], np.cumsum(w)[:-1]]) / w.sum()
+    keep = np.ones(top.size, bool) if p >= 1 else (before < p)
+    keep[0] = True
+    n = int(np.argmin(keep)) if not keep.all() else keep.size
+    return np.sort(top[:n])
+
+
+def pin_mask_vs_numpy(lib: str) -> None:
+    for dist, k, p, scale in (("normal", 20, 0.95, 3.0), ("normal", 1000, 0.5, 1.0),
+                              ("ties", 50, 0.9, 3.0), ("peaked", 20, 0.95, 3.0),
+                              ("normal", 7, 0.3, 0.5)):
+        case = inputs.sampler_case(rows=12, vocab=5000, k=k, p=p, seed=k + int(10 * p),
+                                   scale=scale, dist=dist)
+        z = case.logits + np.float32(0.0)               # -0.0 -> +0.0 (numpy ties them)
+        out, st, kept = oracle.topk_topp_mask(z, case.k, case.p, lib_path=lib)
+        assert np.all(st == 0)
+        for r in range(case.rows):
+            want = _mask_numpy(z[r], int(case.k[r]), float(case.p[r]))
+            got = np.flatnonzero(out[r] != -np.inf)
+            assert np.array_equal(got, want), (dist, k, p, r)
+            assert np.array_equal(out[r, got], z[r, got]) and kept[r] == want.size
+
+
+def pin_mask_closed_forms(lib: str) -> None:
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal((6, 300)).astype(np.float32)
+    # p = 1: exactly the top-k by (logit desc, index asc).
+    out, _, _ = oracle.topk_topp_mask(z, 17, 1.0, lib_path=lib)
+    for r in range(6):
+        want = np.sort(np.argsort(-z[r].astype(np.float64), kind="stable")[:17])
+        assert np.array_equal(np.flatnonzero(out[r] != -np.inf), want)
+    # k = 1 or p = 0: the argmax alone (first index among equal maxima).
+    zz = z.copy()
+    zz[:, 10] = zz[:, 200] = 9.0
+    for k, p in ((1, 0.95), (40, 0.0)):
+        out, _, kept = oracle.topk_topp_mask(zz, k, p, lib_path=lib)
+        assert np.all(kept == 1) and np.all(np.flatnonzero(out.reshape(-1) != -np.inf) % 300 == 10)
+    # A flat row: n equal logits, masses before token i are i/n: ceil(p n) stay.
+    flat = np.zeros((1, 64), np.float32)
+    for k, p in ((64, 0.3), (10, 0.55), (33, 0.99), (5, 0.21)):
+        out, _, kept = oracle.topk_topp_mask(flat, k, p, lib_path=lib)
+        n = math.ceil(p * k)
+        assert kept[0] == n and np.flatnonzero(out[0] == 0).tolist() == list(range(n)), (k, p)
+    # Invalid rows are copied unchanged.
+    out, st, _ = oracle.topk_topp_mask(z[:3], [0, 1025, 5], [0.5, 0.5, np.nan], lib_path=lib)
+    assert st.tolist() == [oracle.MASK_BAD_K, oracle.MASK_BAD_K, oracle.MASK_BAD_P]
+    assert np.array_equal(out, z[:3])
+    _, st, kept = oracle.topk_topp_mask(z[:2], [1024, 1], [1.0, 1.0], lib_path=lib)
+    assert st.tolist() == [0, 0] and kept.tolist() == [300, 1]   # k = k_max is valid
+    # -inf logits rank last; with fewer finite logits than k they fill the set.
+    zi = np.full((1, 8), -np.inf, np.float32)
+    zi[0, [2, 5]] = [1.0, 3.0]
+    out, _, kept = oracle.topk_topp_mask(zi, 4, 1.0, lib_path=lib)
+    assert kept[0] == 4 and out[0, 5] == 3.0 and out[0, 2] == 1.0
+
+
+def pin_mask_invariants(lib: str) -> None:
+    case = inputs.sampler_case(rows=8, vocab=3000, k=64, p=0.9, seed=5, dist="ties")
+    z = case.logits
+    out, _, kept = oracle.topk_topp_mask(z, case.k, case.p, lib_path=lib)
+    # Adding 1 to every logit (exact on the half-integer grid) keeps the mask.
+    out1, _, kept1 = oracle.topk_topp_mask(z + np.float32(1.0), case.k, case.p, lib_path=lib)
+    assert np.array_equal(out1 == -np.inf, out == -np.inf) and np.array_equal(kept, kept1)
+    # Rows are independent.
+    for r in (0, 7):
+        o, _, _ = oracle.topk_topp_mask(z[r:r + 1], case.k[r:r + 1], case.p[r:r + 1],
+                                        lib_path=lib)
+        assert np.array_equal(o[0], out[r])
+    # Moving distinct logits around moves the mask with them.
+    d = inputs.sampler_case(rows=2, vocab=2000, k=30, p=0.8, seed=6).logits
+    assert all(len(np.unique(d[r])) == d.shape[1] for r in range(2))
+    perm = np.random.default_rng(1).permutation(d.shape[1])
+    o0, _, _ = oracle.topk_topp_mask(d, 30, 0.8, lib_path=lib)
+    o1, _, _ = oracle.topk_topp_mask(d[:, perm], 30, 0.8, lib_path=lib)
+    assert np.array_equal(o0[:, perm], o1)
+    # A larger p never keeps fewer tokens; a larger k never fewer either.
+    _, _, ka = oracle.topk_topp_mask(z, 64, 0.5, lib_path=lib)
+    _, _, kb = oracle.topk_topp_mask(z, 64, 0.7, lib_path=lib)
+    _, _, kc = oracle.topk_topp_mask(z, 128, 0.7, lib_path=lib)
+    assert np.all(ka <= kb) and np.all(kb <= kc)
+
+
+def pin_mask_errors(lib: str) -> None:
+    c = oracle.load(lib)
+    z = np.zeros((2, 8), np.float32)
+    o = np.zeros((2, 8), np.float32)
+    k = np.ones(2, np.int32)
+    p = np.ones(2, np.float32)
+    st = np.zeros(2, np.int32)
+    kept = np.zeros(2, np.int32)
+
+    def call(rows=2, V=8, stride=8, ostride=8, k_max=1024):
+        return c.oracle_topk_topp_mask(z.ctypes.data, stride, rows, V, k.ctypes.data,
+                                       p.ctypes.data, k_max, o.ctypes.data, ostride,
+                                       st.ctypes.data, kept.ctypes.data)
+    assert call() == 0
+    for bad in (dict(rows=-1), dict(V=0), dict(stride=7), dict(ostride=7), dict(k_max=0)):
+        assert call(**bad) == oracle.ORACLE_ERR_ARG, bad
+
+
 ALL_PINS = [pin_e4m3_vs_torch, pin_e4m3_golden, pin_f16_vs_numpy, pin_sdpa,
             pin_sparse_vs_masked_sdpa, pin_closed_forms, pin_invariants, pin_errors,
             pin_topk_vs_stable_sort, pin_topk_brute_force, pin_topk_total_order,
             pin_topk_closed_forms, pin_topk_invariants, pin_topk_errors,
             pin_page4_golden, pin_page4_brute_force, pin_page4_attention,
-            pin_page4_invariants, pin_page4_errors]
+            pin_page4_invariants, pin_page4_errors,
+            pin_mask_golden, pin_mask_vs_numpy, pin_mask_closed_forms, pin_mask_invariants,
+            pin_mask_errors]

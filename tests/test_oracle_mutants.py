@@ -71,6 +71,19 @@ MUTANTS = {
                              ";"),
     "page4_page_unchecked": ("if (p < 0 || p >= num_pages) {", "if (p < 0) {"),
     "page4_overflow_unchecked": ("if (n_pages > out_stride) status |= PAGE4_OVERFLOW;", ";"),
+    "mask_norm_over_row": ("for (int32_t i = 0; i < n; ++i) W += exp((double)z[items[i].idx] - m);",
+                           "for (int32_t i = 0; i < V; ++i) W += exp((double)z[items[i].idx] - m);"),
+    "mask_mass_includes_self": ("before += exp((double)z[items[i - 1].idx] - m);",
+                                "before += exp((double)z[items[i].idx] - m);"),
+    "mask_k_ignored": ("const int32_t n = k < V ? k : V;", "const int32_t n = V;"),
+    "mask_p_ignored": ("if (p < 1.0f) {", "if (0) {"),
+    "mask_first_not_kept": ("      keep = 1;\n      for (int32_t i = 1; i < n; ++i) {",
+                            "      keep = 0;\n      for (int32_t i = 1; i < n; ++i) {"),
+    "mask_invalid_masked": ("for (int32_t t = 0; t < V; ++t) o[t] = z[t];",
+                            "for (int32_t t = 0; t < V; ++t) o[t] = -INFINITY;"),
+    "mask_k_bound": ("if (k < 1 || k > k_max) st |= MASK_BAD_K;",
+                     "if (k < 1 || k >= k_max) st |= MASK_BAD_K;"),
+    "mask_p_nan_unchecked": ("if (isnan(p)) st |= MASK_BAD_P;", ";"),
 }
 
 
