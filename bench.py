@@ -223,6 +223,76 @@ def bench_page4(args) -> int:
     return 0
 
 
+def cpu_baseline_sampler(case, budget_s: float) -> dict:
+    """The oracle's masking, as it is, on a bounded sample of rows (doubling
+    from one row until about `budget_s`)."""
+    import oracle
+
+    rows, el = 1, 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.topk_topp_mask(case.logits[:rows], case.k[:rows], case.p[:rows],
+                              k_max=case.k_max)
+        el = time.perf_counter() - t0
+        if el >= budget_s / 3 or rows >= case.rows:
+            break
+        rows = min(case.rows, rows * 2)
+    gbs = rows * case.vocab * 8 / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"first {rows} of {case.rows} rows, {el * 1e3:.1f} ms"}
+
+
+def bench_sampler(args) -> int:
+    """Combined top-k/top-p masking: one step = one sampler_topk_topp_mask
+    call over every row (three kernels).  `value` is the call's algorithmic
+    bytes (every logit read once and written once) per average call time."""
+    import torch
+
+    from fp8_kv_amd import inputs, pgqa
+
+    pgqa.load()
+    torch.cuda.set_device(0)
+    case = inputs.sampler_workload_case(args.workload)
+    R = max(1, args.pools)
+    logits = [torch.from_numpy(case.logits).to("cuda")]
+    for _ in range(R - 1):
+        logits.append(logits[0].clone())
+    k = torch.from_numpy(case.k).to("cuda")
+    p = torch.from_numpy(case.p).to("cuda")
+    out = torch.empty_like(logits[0])
+    st = torch.empty(case.rows, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(8, pgqa.sampler_topk_topp_workspace_bytes(case.rows, case.vocab,
+                                                                   case.k_max)),
+                     dtype=torch.uint8, device="cuda")
+
+    def call(i):
+        pgqa.sampler_topk_topp_mask(logits[i % R], k, p, k_max=case.k_max, out=out, status=st,
+                                    workspace=ws)
+
+    ms = time_steps(call, args.steps, args.warmup, R, not args.eager)
+    alg = case.rows * case.vocab * 8
+    gbs = alg / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "HBM GB/s and µs/call, combined top-k/top-p masking of sampler logits",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "rows": case.rows, "vocab": case.vocab,
+                   "top_k": int(case.k[0]), "top_p": float(case.p[0]), "k_max": case.k_max,
+                   "logit_copies_rotated": R, "us_per_call": round(ms * 1e3, 3),
+                   "alg_bytes_per_call": alg,
+                   "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "chunk_top_kernel + cut_kernel + apply_kernel",
+                     "kernel_us": round(ms * 1e3, 3)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_sampler(case, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def time_steps(step, steps: int, warmup: int, R: int, use_graph: bool) -> float:
     """Average milliseconds per step over exactly `steps` steps, timed with HIP
     events on the stream the kernels run on.  With use_graph the R steps of
@@ -289,6 +359,8 @@ def main() -> int:
         return bench_topk(args)
     if args.workload in inputs.PAGE4_WORKLOADS:
         return bench_page4(args)
+    if args.workload in inputs.SAMPLER_WORKLOADS:
+        return bench_sampler(args)
 
     import torch
 

@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpgqa.so")
-SOURCES = ["pgqa_api.hip", "pgqa_kernels.hip", "qsa_api.hip", "qsa_page4.hip", "qsa_topk.hip"]
+SOURCES = ["pgqa_api.hip", "pgqa_kernels.hip", "qsa_api.hip", "qsa_page4.hip", "qsa_topk.hip",
+           "sampler_api.hip", "sampler_mask.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

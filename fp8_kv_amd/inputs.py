@@ -538,7 +538,7 @@ class SamplerCase:
 
 
 def sampler_case(*, rows: int, vocab: int, k=20, p=0.95, seed: int = 0, scale: float = 3.0,
-                 dist: str = "normal", k_max: int = 1024) -> SamplerCase:
+                 dist: str = "normal", k_max: int = 256) -> SamplerCase:
     """Seeded logits.  dist: "normal" (N(0, scale^2) fp32), "ties" (normal
     rounded to multiples of 1/2, so many tokens share a logit), "flat" (every
     logit 0), "peaked" (normal plus a few tokens raised by 10*scale).  k and p:

@@ -31,13 +31,17 @@ SIZE_MAX = ctypes.c_size_t(-1).value
 EXPORTS = ("paged_gqa_workspace_bytes", "paged_gqa_num_splits", "paged_gqa_decode",
            "paged_gqa_prefill_sparse", "paged_gqa_decode_partial", "paged_gqa_merge_partials",
            "e4m3_decode_table", "qsa_topk_select", "qsa_build_page4_table",
-           "pgqa_error_string")
+           "sampler_topk_topp_workspace_bytes", "sampler_topk_topp_mask", "pgqa_error_string")
 QSA_MAX_BLOCKS = 65536
 QSA_MAX_SEL_TOKENS = 8192
 # Row status bits of qsa_build_page4_table.
 PAGE4_EMPTY, PAGE4_PARTIAL, PAGE4_TAIL, PAGE4_PAGE = 1, 2, 4, 8
 PAGE4_OVERFLOW, PAGE4_SEQ, PAGE4_LONG = 16, 32, 64
 PAGE4_MAX_LIVE = 1 << 26
+SAMPLER_MAX_K = 256
+SAMPLER_MAX_VOCAB = 524288
+# Row status bits of sampler_topk_topp_mask.
+SAMPLER_MASK_BAD_K, SAMPLER_MASK_BAD_P = 1, 2
 
 
 class PgqaError(RuntimeError):
@@ -93,6 +97,11 @@ def _lib(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qsa_build_page4_table.restype = ctypes.c_int
     lib.qsa_build_page4_table.argtypes = [vp, ctypes.c_int64, i32, vp, vp, i32, vp, i32, i32, i32,
                                           i32, i32, vp, i32, vp, vp, vp]
+    lib.sampler_topk_topp_workspace_bytes.restype = sz
+    lib.sampler_topk_topp_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.sampler_topk_topp_mask.restype = ctypes.c_int
+    lib.sampler_topk_topp_mask.argtypes = [vp, ctypes.c_int64, i32, i32, vp, vp, i32, vp,
+                                           ctypes.c_int64, vp, vp, sz, vp]
     lib.pgqa_error_string.restype = ctypes.c_char_p
     lib.pgqa_error_string.argtypes = [ctypes.c_int]
     _LIB = lib
@@ -278,6 +287,43 @@ def qsa_build_page4_table(tokens, live_len, block_table, *, num_pages: int, page
         _ptr(out_len), _ptr(out_status), _stream_handle(stream))
     _check(rc, "qsa_build_page4_table")
     return out_table, out_len, out_status
+
+
+def sampler_topk_topp_workspace_bytes(rows: int, vocab: int, k_max: int = SAMPLER_MAX_K) -> int:
+    r = _lib().sampler_topk_topp_workspace_bytes(int(rows), int(vocab), int(k_max))
+    if r == ctypes.c_size_t(-1).value:
+        raise PgqaError(PGQA_ERR_SHAPE, "sampler_topk_topp_workspace_bytes")
+    return int(r)
+
+
+def sampler_topk_topp_mask(logits, k, p, *, k_max: int = SAMPLER_MAX_K, out=None, status=None,
+                           workspace=None, stream=None):
+    """Combined top-k/top-p masking of fp32 logits [rows][vocab] (see
+    include/pgqa.h).  k: int32 [rows]; p: float32 [rows] (device tensors).
+    out may be `logits` (in place).  Returns (out, status), allocating them
+    and the workspace when not given."""
+    import torch
+
+    if logits.dim() != 2 or logits.dtype != torch.float32 or logits.stride(1) != 1:
+        raise ValueError("logits must be a float32 [rows][vocab] tensor with unit column stride")
+    rows, vocab = logits.shape
+    dev = logits.device
+    if out is None:
+        out = torch.empty_like(logits)
+    if status is None:
+        status = torch.empty(rows, dtype=torch.int32, device=dev)
+    if workspace is None:
+        wsb = sampler_topk_topp_workspace_bytes(rows, vocab, k_max)
+        workspace = torch.empty(max(wsb, 8), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    stride = logits.stride(0) if rows > 1 else vocab
+    ostride = out.stride(0) if rows > 1 else vocab
+    rc = _lib().sampler_topk_topp_mask(_ptr(logits), int(stride), int(rows), int(vocab), _ptr(k),
+                                       _ptr(p), int(k_max), _ptr(out), int(ostride),
+                                       _ptr(status), _ptr(workspace), ws_bytes,
+                                       _stream_handle(stream))
+    _check(rc, "sampler_topk_topp_mask")
+    return out, status
 
 
 # ------------------------------------------------------------ device inputs

@@ -301,6 +301,51 @@ int qsa_build_page4_table(const int32_t* tokens, int64_t token_stride, int32_t n
                           int32_t rows, int32_t* out_table, int32_t out_stride,
                           int32_t* out_len, int32_t* out_status, void* stream);
 
+/*
+ * Combined top-k / top-p masking of sampler logits (source: "[Kernel][SM70]
+ * Scale NVFP4 E4M3 decode batches", Purpose -- combined top-k/top-p masking
+ * for B8/B16 x 248,320 logits -- and Performance contract, whose sampler uses
+ * top-k 20 and top-p 0.95).  Per row r of `vocab` logits with k = k[r] and
+ * p = p[r]:
+ *   order the tokens by (logit descending, index ascending), logits ranked by
+ *   IEEE 754 totalOrder of their fp32 bit patterns; the first min(k, vocab)
+ *   form the top-k set; in that order token i stays iff it is the first or
+ *   the softmax mass (over the top-k set, computed in fp32) of the tokens
+ *   before it is below p; p >= 1 keeps the whole top-k set; p <= 0 keeps the
+ *   first token only.  out[r][t] = logits[r][t] for kept tokens, -inf for
+ *   every other token.  Logits are finite or -inf (NaN and +inf give
+ *   unspecified masks).
+ *
+ *   logits       fp32 [rows][row_stride] (device), 4-byte aligned.
+ *   rows         >= 0 (0: nothing is launched).
+ *   vocab        1 .. SAMPLER_MAX_VOCAB.
+ *   k, p         int32 [rows] and fp32 [rows] (device).  A row with k outside
+ *                [1, k_max] (status SAMPLER_MASK_BAD_K) or p NaN
+ *                (SAMPLER_MASK_BAD_P) is copied to out unchanged.
+ *   k_max        1 .. SAMPLER_MAX_K: the largest k the call accepts; sizes
+ *                the workspace.
+ *   out          fp32 [rows][out_stride] (device); may be `logits` itself
+ *                (in place, with out_stride == row_stride); must not
+ *                otherwise overlap it.
+ *   status       int32 [rows] (device) or NULL: OR of SAMPLER_MASK_* bits.
+ *   workspace    device memory, 8-byte aligned, at least
+ *                sampler_topk_topp_workspace_bytes(rows, vocab, k_max)
+ *                bytes; caller-owned, contents need no initialisation.
+ * Runs three kernels on `stream`; nothing is allocated.
+ * Errors: PGQA_ERR_SHAPE (rows, vocab or k_max out of range), PGQA_ERR_NULL,
+ * PGQA_ERR_LAYOUT (a stride below vocab or a misaligned pointer),
+ * PGQA_ERR_WORKSPACE, PGQA_ERR_HIP.
+ */
+#define SAMPLER_MAX_K 256
+#define SAMPLER_MAX_VOCAB 524288
+#define SAMPLER_MASK_BAD_K 1
+#define SAMPLER_MASK_BAD_P 2
+size_t sampler_topk_topp_workspace_bytes(int32_t rows, int32_t vocab, int32_t k_max);
+int sampler_topk_topp_mask(const float* logits, int64_t row_stride, int32_t rows, int32_t vocab,
+                           const int32_t* k, const float* p, int32_t k_max, float* out,
+                           int64_t out_stride, int32_t* status, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Static description of a return code. */
 const char* pgqa_error_string(int code);
 

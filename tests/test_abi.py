@@ -238,3 +238,48 @@ def test_page4_constants_match_header():
             oracle.PAGE4_OVERFLOW, oracle.PAGE4_SEQ, oracle.PAGE4_LONG) == \
         (pgqa.PAGE4_EMPTY, pgqa.PAGE4_PARTIAL, pgqa.PAGE4_TAIL, pgqa.PAGE4_PAGE,
          pgqa.PAGE4_OVERFLOW, pgqa.PAGE4_SEQ, pgqa.PAGE4_LONG)
+
+
+def test_sampler_validation(lib):
+    """sampler_topk_topp_mask: every rejected call returns before any HIP call."""
+    f = lib.sampler_topk_topp_mask
+    need = lib.sampler_topk_topp_workspace_bytes(4, 1000, 20)
+    assert need < (1 << 40)
+    ok = dict(z=FAKE, stride=1000, rows=4, V=1000, k=FAKE, p=FAKE, kmax=20, out=FAKE,
+              ostride=1000, st=None, ws=FAKE, wsb=need)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["z"], a["stride"], a["rows"], a["V"], a["k"], a["p"], a["kmax"], a["out"],
+                 a["ostride"], a["st"], a["ws"], a["wsb"], None)
+
+    assert call(rows=0) == pgqa.PGQA_OK
+    for bad in (dict(rows=-1), dict(V=0), dict(V=pgqa.SAMPLER_MAX_VOCAB + 1,
+                                              stride=pgqa.SAMPLER_MAX_VOCAB + 1,
+                                              ostride=pgqa.SAMPLER_MAX_VOCAB + 1),
+                dict(kmax=0), dict(kmax=pgqa.SAMPLER_MAX_K + 1)):
+        assert call(**bad) == pgqa.PGQA_ERR_SHAPE, bad
+    for name in ("z", "k", "p", "out"):
+        assert call(**{name: None}) == pgqa.PGQA_ERR_NULL, name
+    assert call(stride=999) == pgqa.PGQA_ERR_LAYOUT
+    assert call(ostride=999) == pgqa.PGQA_ERR_LAYOUT
+    for name in ("z", "k", "p", "out", "st"):
+        assert call(**{name: FAKE + 2}) == pgqa.PGQA_ERR_LAYOUT, name
+    assert call(ws=None) == pgqa.PGQA_ERR_WORKSPACE
+    assert call(wsb=need - 1) == pgqa.PGQA_ERR_WORKSPACE
+    assert call(ws=FAKE + 4) == pgqa.PGQA_ERR_WORKSPACE
+    assert lib.sampler_topk_topp_workspace_bytes(4, 0, 20) == ctypes.c_size_t(-1).value
+    assert lib.sampler_topk_topp_workspace_bytes(4, 1000, 257) == ctypes.c_size_t(-1).value
+
+
+def test_sampler_constants_match_header():
+    text = open(HEADER).read()
+    for name, val in (("SAMPLER_MAX_K", pgqa.SAMPLER_MAX_K),
+                      ("SAMPLER_MAX_VOCAB", pgqa.SAMPLER_MAX_VOCAB),
+                      ("SAMPLER_MASK_BAD_K", pgqa.SAMPLER_MASK_BAD_K),
+                      ("SAMPLER_MASK_BAD_P", pgqa.SAMPLER_MASK_BAD_P)):
+        m = re.search(rf"#define {name} (\d+)", text)
+        assert m and int(m.group(1)) == val, name
+    import oracle
+    assert (oracle.MASK_BAD_K, oracle.MASK_BAD_P) == (pgqa.SAMPLER_MASK_BAD_K,
+                                                      pgqa.SAMPLER_MASK_BAD_P)
