@@ -31,7 +31,7 @@ struct MaskParams {
   int32_t* status;         // [rows] or nullptr
   int32_t chunk;           // logits per chunk (multiple of 1024)
   int32_t n_chunks;        // <= kMaxChunks
-  uint64_t* cand;          // workspace [rows][n_chunks][k_max] chunk top lists
+  uint64_t* cand;          // workspace [rows][k_max][n_chunks] chunk top lists, rank-major
   uint64_t* cut;           // workspace [rows]: last kept (key << 32 | ~index), 0 = copy row
 };
 

@@ -20,11 +20,13 @@
 //      logits, row): the chunk's top min(k, chunk) tokens in order.  A
 //      threshold T from the lane maxima (each of the four waves contributes
 //      ceil(k/4) lanes whose maximum is >= T, so at least k keys are >= T)
-//      leaves a few candidates, which an LDS bitonic sort orders.
-//   2. cut_kernel, one wave per row: a tournament over the <= 64 sorted chunk
-//      lists (each lane holds one list's head; the wave maximum is the next
-//      token) yields the top-k set in order; then the softmax masses in fp32
-//      (exp2 with log2(e) folded in), a wave prefix sum, and the cut.
+//      leaves a few candidates; one wave sorts up to 512 of them in
+//      registers, more (ties, large k) go through an LDS bitonic sort.
+//   2. cut_kernel, one wave per row: the top-k set in order from the <= 64
+//      sorted chunk lists (the list prefixes at or above the k-th largest
+//      list head, sorted in registers; a tournament over the list heads when
+//      there are too many); then the softmax masses in fp32 (exp2 with
+//      log2(e) folded in), a wave prefix sum, and the cut.
 //   3. apply_kernel: out = logit where its value >= cut, else -inf (rows that
 //      are invalid are copied).
 #include <hip/hip_runtime.h>
@@ -82,6 +84,97 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x;
 }
 
+// x from lane (lane ^ M): quad permutes for M = 1, 2, row shifts within 16
+// lanes for M = 4, 8 (lanes with bit M clear read lane + M, the others
+// lane - M), a lane shuffle for 16 and 32.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
+  if constexpr (M == 1 || M == 2) {
+    return __builtin_amdgcn_update_dpp(0u, x, M == 1 ? 0xB1 : 0x4E, 0xF, 0xF, false);
+  } else if constexpr (M == 4 || M == 8) {
+    const uint32_t up = __builtin_amdgcn_update_dpp(0u, x, 0x100 + M, 0xF, 0xF, false);
+    const uint32_t down = __builtin_amdgcn_update_dpp(0u, x, 0x110 + M, 0xF, 0xF, false);
+    return (threadIdx.x & M) ? down : up;
+  } else {
+    return static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), M));
+  }
+}
+
+template <int M>
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t x) {
+  const uint32_t hi = xor_lane<M>(static_cast<uint32_t>(x >> 32));
+  const uint32_t lo = xor_lane<M>(static_cast<uint32_t>(x));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Stages J, J/2, .., 1 of merge level K of a descending bitonic sort of the
+// wave's 64*E values, lane l holding elements l*E .. l*E + E-1.  Element i
+// keeps the larger of its pair when ((i & J) == 0) == ((i & K) == 0).
+template <int E, int K, int J>
+__device__ __forceinline__ void desc_stages(uint64_t (&x)[E]) {
+  if constexpr (J >= 1) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (J < E) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int f = e ^ J;
+        if (f > e) {
+          const bool desc = ((lane * E + e) & K) == 0;
+          const uint64_t a = x[e], b = x[f];
+          const bool swap = desc ? (a < b) : (a > b);
+          x[e] = swap ? b : a;
+          x[f] = swap ? a : b;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = lane * E + e;
+        const uint64_t y = xor_lane_u64<J / E>(x[e]);
+        const bool keep_large = (((i & J) == 0) == ((i & K) == 0));
+        x[e] = keep_large ? (x[e] > y ? x[e] : y) : (x[e] < y ? x[e] : y);
+      }
+    }
+    desc_stages<E, K, J / 2>(x);
+  }
+}
+
+template <int E, int K>
+__device__ __forceinline__ void desc_levels(uint64_t (&x)[E]) {
+  if constexpr (K <= 64 * E) {
+    desc_stages<E, K, K / 2>(x);
+    desc_levels<E, 2 * K>(x);
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&x)[E]) {
+  desc_levels<E, 2>(x);
+}
+
+constexpr int kWaveSortE = 8;  // one wave sorts up to 512 candidates in registers
+
+// One wave's sort of the n_c <= 64 E candidates and the chunk's list: its top
+// kc tokens in order, then zeros up to k.
+template <int E>
+__device__ __forceinline__ void sort_and_write(const uint64_t* cand, uint32_t n_c, int32_t kc,
+                                               int32_t k, uint64_t* dst, int32_t n_chunks) {
+  const int lane = threadIdx.x & 63;
+  uint64_t x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t i = lane * E + e;
+    x[e] = i < n_c ? cand[i] : 0;
+  }
+  wave_sort_desc<E>(x);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int32_t i = lane * E + e;
+    if (i < k) dst[static_cast<int64_t>(i) * n_chunks] = i < kc ? x[e] : 0;
+  }
+  for (int32_t i = 64 * E + lane; i < k; i += 64) dst[static_cast<int64_t>(i) * n_chunks] = 0;
+}
+
 __global__ __launch_bounds__(kThreads) void chunk_top_kernel(MaskParams p) {
   extern __shared__ uint64_t cand[];  // [pow2 >= chunk] candidates, then padding
   __shared__ uint32_t wval[kWaves];
@@ -90,22 +183,27 @@ __global__ __launch_bounds__(kThreads) void chunk_top_kernel(MaskParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  int32_t k;
-  float pp;
-  if (!row_valid(p, row, k, pp)) return;  // the row is copied by apply_kernel
   const int32_t start = chunk * p.chunk;
   const int32_t len = min(p.chunk, p.vocab - start);
-  const int32_t kc = min(k, len);
   const float* src = p.logits + static_cast<int64_t>(row) * p.row_stride + start;
 
   // Thread t holds entries t + 256 i; key 0 (never a logit's key but the
-  // negative NaN 0xFFFFFFFF's) marks entries past the chunk.
+  // negative NaN 0xFFFFFFFF's) marks entries past the chunk.  The loads are
+  // issued before the row's k and p are known.
   uint32_t key[kPerThread];
-  uint32_t lmax = 0;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int32_t e = tid + kThreads * i;
-    key[i] = e < len ? key_of(src[e]) : 0u;
+    key[i] = e < len ? __float_as_uint(src[e]) : 0xFFFFFFFFu;
+  }
+  int32_t k;
+  float pp;
+  if (!row_valid(p, row, k, pp)) return;  // the row is copied by apply_kernel
+  const int32_t kc = min(k, len);
+  uint32_t lmax = 0;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    key[i] = key_of(__uint_as_float(key[i]));  // 0xFFFFFFFF (past the chunk) -> key 0
     lmax = max(lmax, key[i]);
   }
 
@@ -140,6 +238,23 @@ __global__ __launch_bounds__(kThreads) void chunk_top_kernel(MaskParams p) {
     const int32_t e = tid + kThreads * i;
     if (e < len && key[i] >= T) cand[pos++] = token(key[i], start + e);
   }
+  // The chunk's list, rank-major: rank i at dst[i * n_chunks].
+  uint64_t* dst = p.cand + static_cast<int64_t>(row) * p.n_chunks * p.k_max + chunk;
+  if (n_c <= 64 * kWaveSortE) {
+    // Few candidates (the usual case): one wave sorts them in registers and
+    // writes the chunk's list, its top kc tokens in order, then zeros up to k.
+    __syncthreads();
+    if (wave != 0) return;
+    if (n_c <= 64)
+      sort_and_write<1>(cand, n_c, kc, k, dst, p.n_chunks);
+    else if (n_c <= 128)
+      sort_and_write<2>(cand, n_c, kc, k, dst, p.n_chunks);
+    else if (n_c <= 256)
+      sort_and_write<4>(cand, n_c, kc, k, dst, p.n_chunks);
+    else
+      sort_and_write<8>(cand, n_c, kc, k, dst, p.n_chunks);
+    return;
+  }
   uint32_t n2 = 64;
   while (n2 < n_c) n2 <<= 1;
   for (uint32_t i = n_c + tid; i < n2; i += kThreads) cand[i] = 0;
@@ -162,24 +277,57 @@ __global__ __launch_bounds__(kThreads) void chunk_top_kernel(MaskParams p) {
   }
 
   // The chunk's list: its top kc tokens in order, then zeros up to k.
-  uint64_t* dst = p.cand + (static_cast<int64_t>(row) * p.n_chunks + chunk) * p.k_max;
-  for (int32_t i = tid; i < k; i += kThreads) dst[i] = i < kc ? cand[i] : 0;
+  for (int32_t i = tid; i < k; i += kThreads)
+    dst[static_cast<int64_t>(i) * p.n_chunks] = i < kc ? cand[i] : 0;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+// Sorts buf[0 .. cnt) descending in place (one wave, cnt <= 64 E).
+template <int E>
+__device__ __forceinline__ void sort_top(uint64_t* buf, uint32_t cnt) {
+  const int lane = threadIdx.x & 63;
+  uint64_t x[E];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(x >> 32), o));
-    const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), o));
-    const uint64_t y = (static_cast<uint64_t>(hi) << 32) | lo;
-    x = x > y ? x : y;
+  for (int e = 0; e < E; ++e) {
+    const uint32_t i = lane * E + e;
+    x[e] = i < cnt ? buf[i] : 0;
   }
-  return x;
+  wave_sort_desc<E>(x);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t i = lane * E + e;
+    if (i < cnt) buf[i] = x[e];
+  }
+}
+
+// Step of the wave maximum: combine with the lane DPP control `ctrl` names
+// (lanes without a source see 0, the minimum).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void max_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t h2 = __builtin_amdgcn_update_dpp(0u, hi, CTRL, ROWS, 0xF, false);
+  const uint32_t l2 = __builtin_amdgcn_update_dpp(0u, lo, CTRL, ROWS, 0xF, false);
+  const bool take = h2 > hi || (h2 == hi && l2 > lo);
+  hi = take ? h2 : hi;
+  lo = take ? l2 : lo;
+}
+
+// Maximum over the wave's 64 lanes, on every lane: row shifts fold each row
+// of 16 lanes into its lane 15, row broadcasts fold the rows into lane 63.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  uint32_t hi = static_cast<uint32_t>(x >> 32), lo = static_cast<uint32_t>(x);
+  max_step<0x111, 0xF>(hi, lo);  // row_shr:1
+  max_step<0x112, 0xF>(hi, lo);  // row_shr:2
+  max_step<0x114, 0xF>(hi, lo);  // row_shr:4
+  max_step<0x118, 0xF>(hi, lo);  // row_shr:8
+  max_step<0x142, 0xA>(hi, lo);  // row_bcast:15 into rows 1 and 3
+  max_step<0x143, 0xC>(hi, lo);  // row_bcast:31 into rows 2 and 3
+  hi = __builtin_amdgcn_readlane(hi, 63);
+  lo = __builtin_amdgcn_readlane(lo, 63);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 __global__ __launch_bounds__(64) void cut_kernel(MaskParams p) {
-  extern __shared__ uint64_t lists[];  // [n_chunks][k]
-  __shared__ uint64_t top[kMaxK];
+  extern __shared__ uint64_t lists[];  // [k][n_chunks], rank-major
+  __shared__ uint64_t top[64 * kWaveSortE];
   const int row = blockIdx.x;
   const int lane = threadIdx.x;
   int32_t k;
@@ -194,22 +342,64 @@ __global__ __launch_bounds__(64) void cut_kernel(MaskParams p) {
   }
   const int32_t n = min(k, p.vocab);
   // The chunk lists of the row (list j at lists + j * k), loaded together.
+  // The first k ranks of every chunk list are contiguous (rank-major): one
+  // flat coalesced read, 16 loads per lane in flight.
   const uint64_t* src = p.cand + static_cast<int64_t>(row) * p.n_chunks * p.k_max;
-  for (int32_t j = 0; j < p.n_chunks; ++j)
-    for (int32_t i = lane; i < k; i += 64) lists[j * k + i] = src[j * p.k_max + i];
+  const int32_t total = k * p.n_chunks;
+  constexpr int kBatch = 16;
+  for (int32_t e0 = 0; e0 < total; e0 += 64 * kBatch) {
+    uint64_t v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int32_t e = e0 + 64 * u + lane;
+      v[u] = e < total ? src[e] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int32_t e = e0 + 64 * u + lane;
+      if (e < total) lists[e] = v[u];
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
-  // Tournament: lane j holds list j's head; the wave maximum is the next
-  // token in the order.
-  int32_t at = 0;
-  uint64_t head = lane < p.n_chunks ? lists[lane * k] : 0;
-  for (int32_t s = 0; s < n; ++s) {
-    const uint64_t best = wave_max_u64(head);
-    if (lane == 0) top[s] = best;
-    if (head == best) {
-      ++at;
-      head = at < k ? lists[lane * k + at] : 0;
+  // The top-n tokens in order.  The n-th largest list-head key T is a lower
+  // bound for the n-th largest key of the row (n heads reach it), so the
+  // list prefixes with keys >= T hold the top n.  Usually a few dozen: one
+  // wave sorts them in registers.  More than 512 (many equal keys) take a
+  // tournament instead: lane j holds list j's head; the wave maximum is the
+  // next token.
+  const uint64_t head = lane < p.n_chunks ? lists[lane] : 0;
+  uint32_t T = 0;
+  if (n <= p.n_chunks) T = wave_mth_largest(static_cast<uint32_t>(head >> 32), n);
+  int32_t c = 0;
+  if (lane < p.n_chunks)
+    while (c < k && static_cast<uint32_t>(lists[c * p.n_chunks + lane] >> 32) >= T) ++c;
+  const uint32_t cincl = wave_incl_scan(static_cast<uint32_t>(c));
+  const uint32_t total_c = __builtin_amdgcn_readlane(cincl, 63);
+  if (total_c <= 64 * kWaveSortE) {
+    for (int32_t i = 0, pos = static_cast<int32_t>(cincl) - c; i < c; ++i, ++pos)
+      top[pos] = lists[i * p.n_chunks + lane];
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (total_c <= 64)
+      sort_top<1>(top, total_c);
+    else if (total_c <= 128)
+      sort_top<2>(top, total_c);
+    else if (total_c <= 256)
+      sort_top<4>(top, total_c);
+    else
+      sort_top<8>(top, total_c);
+  } else {
+    int32_t at = 0;
+    uint64_t h = head;
+    for (int32_t s = 0; s < n; ++s) {
+      const uint64_t best = wave_max_u64(h);
+      if (lane == 0) top[s] = best;
+      if (h == best) {
+        ++at;
+        h = at < k ? lists[at * p.n_chunks + lane] : 0;
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -254,18 +444,47 @@ __global__ __launch_bounds__(64) void cut_kernel(MaskParams p) {
   }
 }
 
+__device__ __forceinline__ float masked(float z, int32_t t, uint64_t cut) {
+  return (cut == 0 || token(key_of(z), t) >= cut) ? z : -__builtin_huge_valf();
+}
+
+// out = logit where its token value is at or above the row's cut, else -inf;
+// cut 0 copies the row.  VEC: rows 16-byte aligned (strides multiples of 4).
+template <bool VEC>
 __global__ __launch_bounds__(256) void apply_kernel(MaskParams p) {
   const int row = blockIdx.y;
-  const uint64_t cut = p.cut[row];
   const float* src = p.logits + static_cast<int64_t>(row) * p.row_stride;
   float* dst = p.out + static_cast<int64_t>(row) * p.out_stride;
-  const int32_t base = blockIdx.x * (256 * 16);
+  if constexpr (VEC) {
+    const int32_t base = blockIdx.x * (256 * 16);
+    float4 zz[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int32_t t = base + 256 * i + static_cast<int32_t>(threadIdx.x);
-    if (t < p.vocab) {
-      const float z = src[t];
-      dst[t] = (cut == 0 || token(key_of(z), t) >= cut) ? z : -__builtin_huge_valf();
+    for (int i = 0; i < 4; ++i) {
+      const int32_t t = base + 4 * (256 * i + static_cast<int32_t>(threadIdx.x));
+      if (t + 4 <= p.vocab) zz[i] = *reinterpret_cast<const float4*>(src + t);
+    }
+    const uint64_t cut = p.cut[row];  // loaded after the logits: they do not wait for it
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t t = base + 4 * (256 * i + static_cast<int32_t>(threadIdx.x));
+      if (t + 4 <= p.vocab) {
+        float4 z = zz[i];
+        z.x = masked(z.x, t, cut);
+        z.y = masked(z.y, t + 1, cut);
+        z.z = masked(z.z, t + 2, cut);
+        z.w = masked(z.w, t + 3, cut);
+        *reinterpret_cast<float4*>(dst + t) = z;
+      } else {
+        for (int32_t u = t; u < p.vocab; ++u) dst[u] = masked(src[u], u, cut);
+      }
+    }
+  } else {
+    const uint64_t cut = p.cut[row];
+    const int32_t base = blockIdx.x * (256 * 16);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int32_t t = base + 256 * i + static_cast<int32_t>(threadIdx.x);
+      if (t < p.vocab) dst[t] = masked(src[t], t, cut);
     }
   }
 }
@@ -316,7 +535,13 @@ hipError_t launch_mask(const MaskParams& p, hipStream_t stream) {
   }
   hipLaunchKernelGGL(cut_kernel, dim3(p.rows), dim3(64), lds, stream, p);
   const unsigned blocks = static_cast<unsigned>((p.vocab + 256 * 16 - 1) / (256 * 16));
-  hipLaunchKernelGGL(apply_kernel, dim3(blocks, p.rows), dim3(256), 0, stream, p);
+  const bool vec = (reinterpret_cast<uintptr_t>(p.logits) & 15u) == 0 &&
+                   (reinterpret_cast<uintptr_t>(p.out) & 15u) == 0 && p.row_stride % 4 == 0 &&
+                   p.out_stride % 4 == 0;
+  if (vec)
+    hipLaunchKernelGGL(apply_kernel<true>, dim3(blocks, p.rows), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(apply_kernel<false>, dim3(blocks, p.rows), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
