@@ -403,7 +403,8 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   float* so = smem;                           // [NW][group][kLdsRow]
   float* sm = so + NW * group * kLdsRow;      // [NW][16]
   float* sl = sm + NW * 16;                   // [NW][16]
-  int* sflags = reinterpret_cast<int*>(sl + NW * 16);  // [NW] bad-page flags
+  float* swt = sl + NW * 16;                  // [16][NW] merge weights (scale folded in)
+  int* sflags = reinterpret_cast<int*>(swt + NW * 16);  // [NW] bad-page flags
   float l_tot = W.l_run + __shfl_xor(W.l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   const bool wave_bad = __ballot(W.bad) != 0;
@@ -427,37 +428,58 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   if (lane == 0) sflags[wave] = wave_bad ? 1 : 0;
   __syncthreads();
 
-  bool any_bad = false;
+  // Per head: the waves' weights 2^(m_w - M) times the output scale, once;
+  // the items below only read them.
+  if (threadIdx.x < group) {
+    const int h = threadIdx.x;
+    bool any_bad = false;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) any_bad |= sflags[w] != 0;
-  // One item = (head h, four consecutive dims).
-  for (int item = threadIdx.x; item < group * (kHeadDim / 4); item += kNT) {
-    const int h = item / (kHeadDim / 4);
-    const int d = 4 * (item % (kHeadDim / 4));
+    for (int w = 0; w < NW; ++w) any_bad |= sflags[w] != 0;
     float M = -__builtin_huge_valf();
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w * 16 + h]);
-    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    float e[NW];
     float den = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float mw = sm[w * 16 + h];
-      if (mw != -__builtin_huge_valf()) {
-        const float e = __builtin_amdgcn_exp2f(mw - M);
-        const float4 o = *reinterpret_cast<const float4*>(so + (w * group + h) * kLdsRow + d);
-        num.x += e * o.x;
-        num.y += e * o.y;
-        num.z += e * o.z;
-        num.w += e * o.w;
-        den += e * sl[w * 16 + h];
-      }
+      e[w] = mw != -__builtin_huge_valf() ? __builtin_amdgcn_exp2f(mw - M) : 0.f;
+      den += e[w] * sl[w * 16 + h];
     }
     // v_scale applied; an empty range (den = 0) gives zeros; a bad page NaNs.
     const float scale = any_bad ? __builtin_nanf("") : (den > 0.f ? p.v_scale / den : 0.f);
-    num.x *= scale;
-    num.y *= scale;
-    num.z *= scale;
-    num.w *= scale;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) swt[h * NW + w] = e[w] * scale;
+    if (p.partials) {
+      const int64_t oh = static_cast<int64_t>(b) * p.hq + g * group + h;
+      p.ws_lse[oh * p.splits + split] = den > 0.f ? M + __log2f(den) : -__builtin_huge_valf();
+    }
+  }
+  __syncthreads();
+  // One item = (head h, four consecutive dims).
+  for (int item = threadIdx.x; item < group * (kHeadDim / 4); item += kNT) {
+    const int h = item / (kHeadDim / 4);
+    const int d = 4 * (item % (kHeadDim / 4));
+    float wt[NW];
+#pragma unroll
+    for (int w = 0; w < NW; w += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(swt + h * NW + w);
+      wt[w] = v.x;
+      wt[w + 1] = v.y;
+      wt[w + 2] = v.z;
+      wt[w + 3] = v.w;
+    }
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (wt[w] != 0.f || wt[w] != wt[w]) {  // a zero weight adds nothing; NaN propagates
+        const float4 o = *reinterpret_cast<const float4*>(so + (w * group + h) * kLdsRow + d);
+        num.x += wt[w] * o.x;
+        num.y += wt[w] * o.y;
+        num.z += wt[w] * o.z;
+        num.w += wt[w] * o.w;
+      }
+    }
     const int64_t oh = static_cast<int64_t>(b) * p.hq + g * group + h;
     if (!p.partials) {
       u2_t packed;
@@ -466,8 +488,6 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
       *reinterpret_cast<u2_t*>(p.out + oh * kHeadDim + d) = packed;
     } else {
       *reinterpret_cast<float4*>(p.ws_o + (oh * p.splits + split) * kHeadDim + d) = num;
-      if (d == 0)
-        p.ws_lse[oh * p.splits + split] = den > 0.f ? M + __log2f(den) : -__builtin_huge_valf();
     }
   }
 }
@@ -563,7 +583,7 @@ hipError_t launch(const AttnParams& p, hipStream_t stream) {
 }  // namespace
 
 size_t attention_lds_bytes(int group, int waves) {
-  return sizeof(float) * (static_cast<size_t>(waves) * group * kLdsRow + 2 * waves * 16) +
+  return sizeof(float) * (static_cast<size_t>(waves) * group * kLdsRow + 3 * waves * 16) +
          sizeof(int) * waves;
 }
 
