@@ -25,7 +25,7 @@ FLAGS = [
     # them with vector ALU ops every tile.
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     # Leading scalar kernel arguments arrive preloaded in SGPRs.
-    "-mllvm", "-amdgpu-kernarg-preload-count=9",
+    "-mllvm", "-amdgpu-kernarg-preload-count=10",
 ]
 
 

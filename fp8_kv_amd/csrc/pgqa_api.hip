@@ -32,7 +32,9 @@ constexpr int kWaves = PGQA_WAVES_PER_WG;
 // Upper bound on splits (the merge reads every partial of a head).
 constexpr int64_t kMaxSplits = 256;
 constexpr int kChunkAlign = kTile * kWaves;  // split length granularity
+constexpr int kChunkAlignShift = kWaves == 4 ? 6 : 7;
 static_assert(kWaves == 4 || kWaves == 8, "workgroups have 4 or 8 waves");
+static_assert(kChunkAlign == 1 << kChunkAlignShift, "granularity is a power of two");
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
@@ -198,11 +200,21 @@ int run_attention(const void* q, const pgqa_kv_pool* kv, const int32_t* table, i
   if (p.partials) {
     p.ws_o = static_cast<float*>(workspace);
     p.ws_lse = p.ws_o + static_cast<size_t>(n) * hq * plan.splits * kHeadDim;
+    // Unequal lengths: the kernels spread the live tokens over all n*S
+    // workgroup slots of a kv head (the partial layout stays internal).
+    if (n <= pgqa::kBalanceMaxSeqs) p.balance_n = n;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (pgqa::launch_attention(p, fp8, s) != hipSuccess) return PGQA_ERR_HIP;
   if (!p.partials) return PGQA_OK;
   pgqa::MergeParams m{p.ws_o, p.ws_lse, static_cast<int64_t>(n) * hq, plan.splits, p.out};
+  if (p.balance_n > 0) {
+    m.lens = lens;
+    m.n = n;
+    m.hq = hq;
+    m.max_len = max_len;
+    m.a_shift = kChunkAlignShift;
+  }
   return pgqa::launch_merge(m, s) == hipSuccess ? PGQA_OK : PGQA_ERR_HIP;
 }
 

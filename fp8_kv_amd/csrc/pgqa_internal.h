@@ -11,6 +11,7 @@ constexpr int kHeadDim = 256;   // head dimension the kernels are built for
 constexpr int kTile = 16;       // tokens per wave tile (one MFMA M/K block)
 constexpr int kMaxWaves = 8;    // waves per workgroup (4 or 8), each on its own tiles
 constexpr int kMaxGroup = 16;   // query heads per kv head (MFMA N = 16)
+constexpr int kBalanceMaxSeqs = 512;  // sequences a balanced (ragged) plan covers
 
 // Everything a launch needs; strides already converted to bytes.
 struct AttnParams {
@@ -36,6 +37,8 @@ struct AttnParams {
   int32_t splits;          // key-range splits per (sequence, kv head)
   int32_t chunk;           // tokens per split, multiple of kTile * waves
   int32_t waves;           // waves per workgroup: 4 or 8
+  int32_t balance_n;       // n > 0: spread unequal lengths over the n*splits slots
+                           // (split partials only, n <= kBalanceMaxSeqs); 0: static
   bool partials;           // write split partials (ws_o, ws_lse) instead of out
   bool stream_kv;          // non-temporal K/V loads (each byte read once per call)
   uint16_t* out;           // fp16 bits [n][hq][256]
@@ -50,6 +53,13 @@ struct MergeParams {
   int64_t rows;
   int32_t splits;
   uint16_t* out;           // fp16 bits [rows][256]
+  // Balanced layout of a whole decode call (see attention): the lengths the
+  // attention launch planned with, else nullptr for the static layout.
+  const int32_t* lens;     // [n]
+  int32_t n;               // sequences (rows = n * hq)
+  int32_t hq;
+  int32_t max_len;
+  int32_t a_shift;         // log2 of the split granularity
 };
 
 hipError_t launch_attention(const AttnParams& p, bool fp8, hipStream_t stream);

@@ -15,6 +15,9 @@
 // b, kv head g, split s): the tokens [s*chunk, min((s+1)*chunk, L_b)).  Wave
 // w takes the 16-token tiles w, w+4, w+8, ... of that range and keeps its own
 // online-softmax state; the four states are merged through LDS at the end.
+// In a whole call with unequal lengths the n*S workgroups of a kv head are
+// re-dealt by length (the balanced plan below), so short sequences leave no
+// workgroup idle.
 // With one split the workgroup writes the fp16 output; with several it writes
 // a normalised fp32 partial and its base-2 log-sum-exp, merged by merge_kernel
 // in a second launch (a kernel boundary makes the partials visible; fencing
@@ -61,6 +64,145 @@ constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the merge buffer
 #ifndef PGQA_PAGE_LOOKAHEAD
 #define PGQA_PAGE_LOOKAHEAD 1
 #endif
+
+// ------------------------------------------------------------ ragged balance
+// A whole decode call over sequences of unequal length spreads the live tokens
+// of each kv head evenly over its n*S workgroup slots.  All sequences share one
+// chunk length c = m*A (A = the split granularity, a power of two): the
+// smallest with sum_b ceil(L_b / c) <= n*S.  Sequence b then owns the
+// ceil(L_b / c) consecutive chunk indices after those of sequences 0..b-1,
+// and chunk index J is stored in partial slot (J / S, J % S), i.e. where the
+// static plan keeps split J % S of sequence J / S.  When every L_b equals
+// max_len the plan is the static one (sequence b owns J = b*S .. b*S + S-1),
+// which both kernels detect before any division.
+//
+// Lengths live in registers of one wave: lane l holds sequences t*64 + l for
+// t < ceil(n / 64); every wave that needs the plan computes it itself.
+constexpr int kBalancePer = kBalanceMaxSeqs / 64;
+
+// Inclusive prefix sum over the 64 lanes (DPP row shifts, then the two row
+// broadcasts that carry rows 0 and 0..1 into the rows above them).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
+}
+
+struct Balance {
+  int L[kBalancePer];  // clamped lengths (0 past n)
+  int u[kBalancePer];  // the same in units of A, rounded up
+  int rows;            // ceil(n / 64)
+  bool full;           // every L_b == max_len: the static plan
+};
+
+// Issue the loads of the raw lengths (kept apart from balance_finish so they
+// overlap other loads).
+__device__ __forceinline__ void balance_load(int (&raw)[kBalancePer], const int32_t* lens, int n,
+                                             int lane) {
+#pragma unroll
+  for (int t = 0; t < kBalancePer; ++t) {
+    raw[t] = 0;
+    if (t * 64 < n && t * 64 + lane < n) raw[t] = lens[t * 64 + lane];
+  }
+}
+
+__device__ __forceinline__ Balance balance_finish(const int (&raw)[kBalancePer], int n,
+                                                  int max_len, int a_shift, int lane) {
+  Balance B;
+  B.rows = (n + 63) >> 6;
+  bool short_seq = false;
+#pragma unroll
+  for (int t = 0; t < kBalancePer; ++t) {
+    const bool in = t * 64 + lane < n;
+    const int L = in ? max(0, min(raw[t], max_len)) : 0;
+    B.L[t] = L;
+    B.u[t] = (L + (1 << a_shift) - 1) >> a_shift;
+    short_seq |= in & (L != max_len);
+  }
+  B.full = __ballot(short_seq) == 0;
+  return B;
+}
+
+// The chunk length in units of A (0 when no sequence has a live token).
+// ceil(U / slots) <= m <= ceil(U / (slots - nonempty)) bounds the search:
+// sum_b ceil(u_b / m) < U/m + nonempty, so the upper end always fits.
+// Requires slots > n (S >= 2).
+__device__ __forceinline__ int balance_units(const Balance& B, int slots) {
+  int su = 0, sne = 0;
+#pragma unroll
+  for (int t = 0; t < kBalancePer; ++t)
+    if (t < B.rows) {
+      su += B.u[t];
+      sne += B.u[t] > 0 ? 1 : 0;
+    }
+  const int U = wave_sum(su);
+  const int nne = wave_sum(sne);
+  if (U == 0) return 0;
+  int lo = max(1, (U + slots - 1) / slots);
+  int hi = (U + (slots - nne) - 1) / (slots - nne);
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    int c = 0;
+#pragma unroll
+    for (int t = 0; t < kBalancePer; ++t)
+      if (t < B.rows) c += (B.u[t] + mid - 1) / mid;
+    if (wave_sum(c) <= slots) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+// Chunk index J -> (sequence, chunk within it, its clamped length).  False
+// when J is past the last chunk (the slot has no work).
+__device__ __forceinline__ bool balance_locate(const Balance& B, int m, int J, int& seq,
+                                               int& k, int& L) {
+  int base = 0;
+#pragma unroll
+  for (int t = 0; t < kBalancePer; ++t)
+    if (t < B.rows) {
+      const int nb = (B.u[t] + m - 1) / m;
+      const int incl = wave_incl_scan(nb);
+      const int tot = __builtin_amdgcn_readlane(incl, 63);
+      if (J < base + tot) {
+        const uint64_t own = __ballot((J < base + incl) & (J >= base + incl - nb));
+        const int lo = __builtin_ctzll(own);
+        seq = t * 64 + lo;
+        k = J - base - __builtin_amdgcn_readlane(incl - nb, lo);
+        L = __builtin_amdgcn_readlane(B.L[t], lo);
+        return true;
+      }
+      base += tot;
+    }
+  return false;
+}
+
+// Sequence -> its first chunk index and chunk count.
+__device__ __forceinline__ void balance_range(const Balance& B, int m, int seq, int& start,
+                                              int& cnt) {
+  int base = 0;
+  start = 0;
+  cnt = 0;
+#pragma unroll
+  for (int t = 0; t < kBalancePer; ++t)
+    if (t < B.rows) {
+      const int nb = (B.u[t] + m - 1) / m;
+      const int incl = wave_incl_scan(nb);
+      if ((seq >> 6) == t) {
+        const int lo = seq & 63;
+        start = base + __builtin_amdgcn_readlane(incl - nb, lo);
+        cnt = __builtin_amdgcn_readlane(nb, lo);
+      }
+      base += __builtin_amdgcn_readlane(incl, 63);
+    }
+}
 
 // ------------------------------------------------------------ E4M3 decode
 // Two E4M3 codes (bytes 2*HI, 2*HI+1 of w) to two fp16 values.  Every E4M3
@@ -154,6 +296,21 @@ struct Wave {
 
   __device__ __forceinline__ int tile_start(int k) const {
     return s0 + (wave + NW * k) * kTile;
+  }
+
+  // q^T operand of sequence b, kv head g: head r of the group (zero past the
+  // group), the head-dim pieces in the same permuted order as the K operand.
+  __device__ __forceinline__ void load_q(int b, int g) {
+    const int head = g * p.group + r;
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(
+        p.q + (static_cast<int64_t>(b) * p.hq + (r < p.group ? head : 0)) * kHeadDim);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int d0 = FP8 ? 16 * (qd + 4 * (st >> 1)) + 8 * (st & 1) : 8 * (qd + 4 * st);
+      u4_t v = load16(qrow + 2 * d0);
+      if (r >= p.group) v = u4_t{0u, 0u, 0u, 0u};
+      qop[st] = __builtin_bit_cast(h8_t, v);
+    }
   }
 
   // Page-table entry (and slot) for this lane's K token of tile k.  The token
@@ -290,14 +447,16 @@ struct Wave {
 
 constexpr int gcd_const(int a, int b) { return b == 0 ? a : gcd_const(b, a % b); }
 
-// The leading scalar arguments are what the first page-table load depends on;
-// the library is built with kernel-argument preloading, so they arrive in
-// SGPRs at wave launch and that load does not wait for the parameter block
-// (which is fetched from memory in parallel).
+// The leading scalar arguments are what the first page-table and length loads
+// depend on (bal_n = n selects the balanced plan, 0 the static one); the
+// library is built with kernel-argument preloading, so they arrive in SGPRs at
+// wave launch and those loads do not wait for the parameter block (which is
+// fetched from memory in parallel).
 template <bool FP8, int NW, int PD, int PL, bool NT>
 __global__ __launch_bounds__(64 * NW) void attention_kernel(
     const int32_t* table, const int32_t* lens, int32_t max_pages, int32_t max_len, int32_t chunk,
-    int32_t splits, int32_t hkv, int32_t page_size, float inv_page_size, AttnParams p) {
+    int32_t splits, int32_t hkv, int32_t page_size, float inv_page_size, int32_t bal_n,
+    AttnParams p) {
   p.table = table;
   p.lens = lens;
   p.max_pages = max_pages;
@@ -316,11 +475,20 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   const int wg = blockIdx.x;
   const int split = wg % p.splits;
   const int bg = wg / p.splits;
-  const int b = bg / p.hkv;
+  int b = bg / p.hkv;
   const int g = bg - b * p.hkv;
 
-  const int Lraw = p.lens[b];  // its load overlaps the page-table prefetch below
-  const int s0 = split * p.chunk;
+  // The static plan: split `split` of sequence b.  Its page-table entries are
+  // fetched before the lengths arrive; a balanced plan (bal_n = n > 0) that
+  // moves this workgroup elsewhere fetches them again.
+  int Lraw = p.lens[b];  // its load overlaps the page-table prefetch below
+  int s0 = split * p.chunk;
+  int chunk_len = p.chunk;
+  // Partial slot (split partials only): (b, split) here, and in a balanced
+  // plan too, where this workgroup's chunk index is J = b*S + split.
+  const int slot_row = b, slot_col = split;
+  int raw[kBalancePer];
+  if (bal_n > 0) balance_load(raw, p.lens, bal_n, lane);
 
   Wave<FP8, NW, NT> W{p};
   W.tab = p.table + static_cast<int64_t>(b) * p.max_pages;
@@ -342,28 +510,37 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
 #pragma unroll
   for (int t = 0; t <= PD - 2 + PL; ++t) pg[t % RP] = W.fetch_page(t, ps[t % RP]);
 
-  // q^T operand: head r of the group (zero past the group), the head-dim
-  // pieces in the same permuted order as the K operand.
-  {
-    const int head = g * p.group + W.r;
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(
-        p.q + (static_cast<int64_t>(b) * p.hq + (W.r < p.group ? head : 0)) * kHeadDim);
+  if (bal_n > 0) {
+    const Balance B = balance_finish(raw, bal_n, p.max_len, __builtin_ctz(kTile * NW), lane);
+    if (!B.full) {
+      const int J = b * p.splits + split;
+      const int m = balance_units(B, bal_n * p.splits);
+      int seq, k, L;
+      if (m == 0 || !balance_locate(B, m, J, seq, k, L)) return;  // a slot with no chunk
+      chunk_len = m * kTile * NW;
+      const int s0n = k * chunk_len;
+      if (seq != b) W.tab = p.table + static_cast<int64_t>(seq) * p.max_pages;
+      if (seq != b || s0n != s0) {
+        W.s0 = s0n;
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const int d0 = FP8 ? 16 * (W.qd + 4 * (st >> 1)) + 8 * (st & 1) : 8 * (W.qd + 4 * st);
-      u4_t v = load16(qrow + 2 * d0);
-      if (W.r >= p.group) v = u4_t{0u, 0u, 0u, 0u};
-      W.qop[st] = __builtin_bit_cast(h8_t, v);
+        for (int t = 0; t <= PD - 2 + PL; ++t) pg[t % RP] = W.fetch_page(t, ps[t % RP]);
+      }
+      b = seq;
+      s0 = s0n;
+      Lraw = L;
     }
   }
+  // Loaded once the sequence is settled; the first tile waits for its K/V
+  // loads, issued after these, so this latency is hidden behind theirs.
+  W.load_q(b, g);
 
   const int L = min(Lraw, p.max_len);
-  const int s1 = min(s0 + p.chunk, L);
+  const int s1 = min(s0 + chunk_len, L);
   if (p.partials && s0 >= L) {
     // A split with no live token: its partial is empty (lse = -inf).
     if (threadIdx.x < p.group) {
-      const int64_t oh = static_cast<int64_t>(b) * p.hq + g * p.group + threadIdx.x;
-      p.ws_lse[oh * p.splits + split] = -__builtin_huge_valf();
+      const int64_t oh = static_cast<int64_t>(slot_row) * p.hq + g * p.group + threadIdx.x;
+      p.ws_lse[oh * p.splits + slot_col] = -__builtin_huge_valf();
     }
     return;
   }
@@ -451,8 +628,8 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
 #pragma unroll
     for (int w = 0; w < NW; ++w) swt[h * NW + w] = e[w] * scale;
     if (p.partials) {
-      const int64_t oh = static_cast<int64_t>(b) * p.hq + g * group + h;
-      p.ws_lse[oh * p.splits + split] = den > 0.f ? M + __log2f(den) : -__builtin_huge_valf();
+      const int64_t oh = static_cast<int64_t>(slot_row) * p.hq + g * group + h;
+      p.ws_lse[oh * p.splits + slot_col] = den > 0.f ? M + __log2f(den) : -__builtin_huge_valf();
     }
   }
   __syncthreads();
@@ -480,14 +657,15 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
         num.w += wt[w] * o.w;
       }
     }
-    const int64_t oh = static_cast<int64_t>(b) * p.hq + g * group + h;
     if (!p.partials) {
+      const int64_t oh = static_cast<int64_t>(b) * p.hq + g * group + h;
       u2_t packed;
       packed[0] = f16_bits(num.x) | (static_cast<uint32_t>(f16_bits(num.y)) << 16);
       packed[1] = f16_bits(num.z) | (static_cast<uint32_t>(f16_bits(num.w)) << 16);
       *reinterpret_cast<u2_t*>(p.out + oh * kHeadDim + d) = packed;
     } else {
-      *reinterpret_cast<float4*>(p.ws_o + (oh * p.splits + split) * kHeadDim + d) = num;
+      const int64_t oh = static_cast<int64_t>(slot_row) * p.hq + g * group + h;
+      *reinterpret_cast<float4*>(p.ws_o + (oh * p.splits + slot_col) * kHeadDim + d) = num;
     }
   }
 }
@@ -497,27 +675,82 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
 // a split with lse = -inf (no live token) has weight 0 and its stored output
 // is not used.  The lse values and the partial outputs of a chunk of 32
 // splits are loaded together, so a chunk costs about one memory round trip.
+//
+// Static layout (lens = nullptr): row r's partials are slots r*S .. r*S+S-1.
+// Balanced layout (a whole decode call, rows = (sequence b, query head h)):
+// the row's chunk indices J come from the plan above and live in slots
+// ((J / S) * hq + h) * S + J % S.  The first chunk is loaded at the static
+// slots while the lengths are in flight; it is loaded again only if the plan
+// is not the static one.
 __global__ __launch_bounds__(64) void merge_kernel(const float* lse_base, const float* o_base,
-                                                   int32_t splits, MergeParams p) {
+                                                   int32_t splits, const int32_t* lens,
+                                                   int32_t n, int32_t hq_in, MergeParams p) {
   p.lse = lse_base;  // leading arguments: preloaded into SGPRs
   p.o = o_base;
   p.splits = splits;
+  p.lens = lens;
+  p.n = n;
+  p.hq = hq_in;
   constexpr int kChunk = 32;
-  const int64_t row = blockIdx.x;
+  const int S = p.splits;
   const int lane = threadIdx.x;
-  const float* lse = p.lse + row * p.splits;
-  const float4* po =
-      reinterpret_cast<const float4*>(p.o + row * p.splits * kHeadDim) + lane;
+  const int hq = p.lens ? p.hq : 1;
+  const int row = blockIdx.x;
+  const int b = row / hq;
+  const int h = row - b * hq;
+  int raw[kBalancePer];
+  if (p.lens) balance_load(raw, p.lens, p.n, lane);
+  const float4* po = reinterpret_cast<const float4*>(p.o) + lane;
+
+  float4 v[kChunk];
+  float l;
+  // Chunk indices j0 .. j0+count-1 (count <= kChunk) into v (and this lane's
+  // lse into l, -inf past count).
+  auto load_chunk = [&](int j0, int count) {
+    int q = j0 / S, r = j0 - q * S;
+    if (r + count <= S) {  // one run of consecutive slots
+      const int64_t base = (static_cast<int64_t>(q) * hq + h) * S + r;
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u)
+        v[u] = u < count ? po[(base + u) * (kHeadDim / 4)] : make_float4(0.f, 0.f, 0.f, 0.f);
+      l = lane < count ? p.lse[base + lane] : -__builtin_huge_valf();
+    } else {
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const int64_t slot = (static_cast<int64_t>(q) * hq + h) * S + r;
+        v[u] = u < count ? po[slot * (kHeadDim / 4)] : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (++r == S) {
+          r = 0;
+          ++q;
+        }
+      }
+      const int jl = j0 + lane;
+      const int ql = jl / S;
+      l = lane < count ? p.lse[(static_cast<int64_t>(ql) * hq + h) * S + (jl - ql * S)]
+                       : -__builtin_huge_valf();
+    }
+  };
+
+  int start = b * S, cnt = S;
+  load_chunk(start, min(cnt, kChunk));
+  bool reload = false;
+  if (p.lens) {
+    const Balance B = balance_finish(raw, p.n, p.max_len, p.a_shift, lane);
+    if (!B.full) {
+      const int m = balance_units(B, p.n * S);
+      int st = 0, c = 0;
+      if (m > 0) balance_range(B, m, b, st, c);
+      reload = st != start || c > S;
+      if (!reload && c < cnt) l = lane < c ? l : -__builtin_huge_valf();
+      start = st;
+      cnt = c;
+    }
+  }
+
   float M = -__builtin_huge_valf(), den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = 0; c0 < p.splits; c0 += kChunk) {
-    float4 v[kChunk];
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u)
-      v[u] = (c0 + u < p.splits) ? po[static_cast<int64_t>(c0 + u) * (kHeadDim / 4)]
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float l = (lane < kChunk && c0 + lane < p.splits) ? lse[c0 + lane]
-                                                           : -__builtin_huge_valf();
+  for (int c0 = 0; c0 < cnt; c0 += kChunk) {
+    if (c0 > 0 || reload) load_chunk(start + c0, min(cnt - c0, kChunk));
     float mc = l;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mc = fmaxf(mc, __shfl_xor(mc, o));
@@ -546,7 +779,7 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* lse_base, const 
     M = m_new;
   }
   const float scale = den > 0.f ? 1.f / den : 0.f;
-  uint16_t* op = p.out + row * kHeadDim + 4 * lane;
+  uint16_t* op = p.out + static_cast<int64_t>(row) * kHeadDim + 4 * lane;
   u2_t packed;
   packed[0] = f16_bits(acc.x * scale) | (static_cast<uint32_t>(f16_bits(acc.y * scale)) << 16);
   packed[1] = f16_bits(acc.z * scale) | (static_cast<uint32_t>(f16_bits(acc.w * scale)) << 16);
@@ -576,7 +809,7 @@ hipError_t launch(const AttnParams& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.splits) * p.n * p.hkv);
   hipLaunchKernelGGL((attention_kernel<FP8, NW, PD, PL, NT>), grid, dim3(64 * NW), lds, stream,
                      p.table, p.lens, p.max_pages, p.max_len, p.chunk, p.splits, p.hkv,
-                     p.page_size, p.inv_page_size, p);
+                     p.page_size, p.inv_page_size, p.balance_n, p);
   return hipGetLastError();
 }
 
@@ -604,7 +837,7 @@ hipError_t launch_attention(const AttnParams& p, bool fp8, hipStream_t stream) {
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(p.rows)), dim3(64), 0, stream, p.lse,
-                     p.o, p.splits, p);
+                     p.o, p.splits, p.lens, p.n, p.hq, p);
   return hipGetLastError();
 }
 

@@ -111,7 +111,9 @@ int32_t paged_gqa_num_splits(int32_t n, int32_t num_kv_heads, int32_t max_seq_le
  * q          : fp16 [batch][num_q_heads][256], contiguous, 16-byte aligned.
  * kv         : host pointer to the pool description (read during the call only).
  * page_table : int32 [batch][max_pages], row-major; only the first
- *              ceil(min(L_b, max_seq_len) / page_size) entries of row b are read.
+ *              ceil(min(L_b, max_seq_len) / page_size) entries of row b are
+ *              used (entries up to ceil(max_seq_len / page_size) may be read
+ *              ahead and ignored, so they need not hold valid page ids).
  *              An entry outside [0, num_pages) is never dereferenced: the
  *              affected output row becomes NaN instead.
  * seq_lens   : int32 [batch]; L_b <= 0 gives zeros; L_b is clamped to max_seq_len.
@@ -124,9 +126,16 @@ int32_t paged_gqa_num_splits(int32_t n, int32_t num_kv_heads, int32_t max_seq_le
  * num_splits : number of key-range splits per (sequence, kv head), 0 = auto;
  *              capped at 256 and at one split per 64 tokens (query the
  *              effective count with paged_gqa_num_splits).
- *              With more than one split the call runs as
- *              paged_gqa_decode_partial into `workspace` followed by
- *              paged_gqa_merge_partials, both enqueued on `stream`.
+ *              With more than one split the call writes split partials into
+ *              `workspace` and merges them (two launches on `stream`).  When
+ *              every L_b >= max_seq_len (or batch > 512) the splits are those
+ *              of paged_gqa_decode_partial and the result equals it followed
+ *              by paged_gqa_merge_partials bit for bit.  Otherwise the
+ *              batch * S workgroup slots of each kv head are shared out by
+ *              length: one chunk length C (a multiple of 64) for all
+ *              sequences, the smallest with sum_b ceil(L_b / C) <= batch * S,
+ *              sequence b taking ceil(L_b / C) chunks, so that unequal
+ *              lengths keep every workgroup equally busy.
  * out        : fp16 [batch][num_q_heads][256], contiguous, 16-byte aligned;
  *              must not alias q.
  * workspace  : device scratch of at least paged_gqa_workspace_bytes(...) bytes

@@ -292,27 +292,84 @@ def test_reused_workspace_and_empty_rows(pg):
 
 @pytest.mark.parametrize("splits", [2, 5, 0])
 def test_partial_then_merge_equals_decode_bitwise(pg, splits):
+    """With every length at (or clamped to) max_seq_len a whole call uses the
+    static split plan, so it equals decode_partial + merge_partials bit for
+    bit; with unequal lengths the two-stage call keeps the static plan (empty
+    splits marked -inf) and still matches the oracle."""
     import torch
 
-    case = inputs.decode_case(batch=3, lens=[4000, 1, 2500], page_size=128, kv_dtype=E4M3,
-                              seed=76, scales="uniform")
-    q, pool, table, lens = pg.device_case(case)
-    n, hq, _ = q.shape
-    S = pg.paged_gqa_num_splits(n, 1, case.max_seq_len, splits)
-    po = torch.empty((n, hq, S, 256), dtype=torch.float32, device="cuda")
-    pl = torch.empty((n, hq, S), dtype=torch.float32, device="cuda")
-    pg.paged_gqa_decode_partial(q, pool, table, lens, case.max_seq_len, case.sm_scale, po, pl,
-                                num_splits=splits)
-    merged = torch.empty_like(q)
-    pg.paged_gqa_merge_partials(po, pl, merged)
-    direct = pg.run_case(case, num_splits=splits)
-    torch.cuda.synchronize()
-    if S > 1:
-        assert torch.equal(merged, direct)
-    # Splits past a sequence's end are marked empty.
-    lse = pl.cpu().numpy()
-    assert np.all(np.isneginf(lse[1, :, 1:]))
-    assert np.all(np.isfinite(lse[1, :, 0]))
+    for lens, max_len in (([4000, 5000, 4000], 4000), ([4000, 1, 2500], None)):
+        case = inputs.decode_case(batch=3, lens=lens, page_size=128, kv_dtype=E4M3,
+                                  seed=76, scales="uniform", max_seq_len=max_len)
+        q, pool, table, d_lens = pg.device_case(case)
+        n, hq, _ = q.shape
+        S = pg.paged_gqa_num_splits(n, 1, case.max_seq_len, splits)
+        po = torch.empty((n, hq, S, 256), dtype=torch.float32, device="cuda")
+        pl = torch.empty((n, hq, S), dtype=torch.float32, device="cuda")
+        pg.paged_gqa_decode_partial(q, pool, table, d_lens, case.max_seq_len, case.sm_scale,
+                                    po, pl, num_splits=splits)
+        merged = torch.empty_like(q)
+        pg.paged_gqa_merge_partials(po, pl, merged)
+        direct = pg.run_case(case, num_splits=splits)
+        torch.cuda.synchronize()
+        clamped = dataclasses.replace(
+            case, lens=np.minimum(case.lens, case.max_seq_len).astype(np.int32))
+        ref = oracle.paged_gqa(**clamped.oracle_kwargs())
+        assert_parity(merged.cpu().numpy(), ref, f"two-stage lens {lens}")
+        if max_len is not None and S > 1:
+            assert torch.equal(merged, direct)
+        if max_len is None:
+            # Splits past a sequence's end are marked empty.
+            lse = pl.cpu().numpy()
+            assert np.all(np.isneginf(lse[1, :, 1:]))
+            assert np.all(np.isfinite(lse[1, :, 0]))
+
+
+# ------------------------------------------- unequal lengths (balanced plan)
+@pytest.mark.parametrize("lens", [
+    [16384] + [0] * 15,          # one sequence takes every slot (> S chunks)
+    [1] * 15 + [16384],
+    [16384] * 15 + [16000],      # all but one at max_seq_len
+    [0, -5, 3, 64, 65, 8191, 16384, 20000] * 2,
+])
+def test_balanced_extremes(pg, lens):
+    case = inputs.decode_case(batch=len(lens), lens=lens, page_size=128, kv_dtype=E4M3,
+                              seed=90 + len(set(lens)), scales="uniform", max_seq_len=16384)
+    clamped = dataclasses.replace(case, lens=np.minimum(case.lens, 16384).astype(np.int32))
+    ref = oracle.paged_gqa(**clamped.oracle_kwargs())
+    for s in (0, 3):
+        assert_parity(_run(pg, case, num_splits=s), ref, f"balanced {lens[:4]} splits {s}")
+
+
+@pytest.mark.parametrize("batch,splits", [(100, 0), (300, 4), (512, 2), (513, 2)])
+def test_balanced_many_sequences(pg, batch, splits):
+    """Plans over 2 .. 8 rows of 64 lengths per wave; 513 sequences keep the
+    static plan."""
+    rng = np.random.default_rng(batch)
+    lens = rng.integers(-2, 700, size=batch)
+    lens[rng.integers(0, batch, size=batch // 10)] = 0
+    case = inputs.decode_case(batch=batch, lens=lens, page_size=16, kv_dtype=FP16,
+                              seed=batch, max_seq_len=700)
+    got = _check(pg, case, f"batch {batch} splits {splits}", num_splits=splits)
+    assert np.all(got[lens <= 0] == 0)
+
+
+def test_balanced_multi_kv_head(pg):
+    case = inputs.decode_case(batch=5, lens=[3000, 10, 0, 2999, 64], page_size=64,
+                              kv_dtype=E4M3, num_q_heads=12, num_kv_heads=2, seed=95,
+                              scales="uniform", max_seq_len=4096)
+    for s in (0, 2, 7):
+        _check(pg, case, f"hkv2 balanced splits {s}", num_splits=s)
+
+
+def test_balanced_all_empty_and_repeat(pg):
+    case = inputs.decode_case(batch=6, lens=[0, 0, -1, 0, 0, 0], page_size=16, kv_dtype=FP16,
+                              seed=96, max_seq_len=256)
+    assert np.all(_run(pg, case, num_splits=4) == 0)
+    case = inputs.workload_case("decode_ragged_b16_16k_p256")
+    a = _run(pg, case)
+    b = _run(pg, case)
+    assert np.array_equal(a, b)
 
 
 def test_merge_of_shards_equals_whole_sequence(pg):
