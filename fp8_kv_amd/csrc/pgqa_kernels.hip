@@ -42,6 +42,8 @@
 //     MFMAs take the dims of those bytes in turn; a byte permute per pair of
 //     tokens builds each operand.  Output dim d of MFMA j, slot m is
 //     16*m + j (FP8) or 128*(j/8) + 8*m + j%8 (FP16).
+#include <type_traits>
+
 #include "pgqa_internal.h"
 
 namespace pgqa {
@@ -105,12 +107,15 @@ struct Balance {
 
 // Issue the loads of the raw lengths (kept apart from balance_finish so they
 // overlap other loads).
+// n >= 1.  Lanes past n re-read the last length (balance_finish ignores
+// them), so the first row is one unconditional load.
 __device__ __forceinline__ void balance_load(int (&raw)[kBalancePer], const int32_t* lens, int n,
                                              int lane) {
+  raw[0] = lens[min(lane, n - 1)];
 #pragma unroll
-  for (int t = 0; t < kBalancePer; ++t) {
+  for (int t = 1; t < kBalancePer; ++t) {
     raw[t] = 0;
-    if (t * 64 < n && t * 64 + lane < n) raw[t] = lens[t * 64 + lane];
+    if (t * 64 < n) raw[t] = lens[min(t * 64 + lane, n - 1)];
   }
 }
 
@@ -121,11 +126,15 @@ __device__ __forceinline__ Balance balance_finish(const int (&raw)[kBalancePer],
   bool short_seq = false;
 #pragma unroll
   for (int t = 0; t < kBalancePer; ++t) {
-    const bool in = t * 64 + lane < n;
-    const int L = in ? max(0, min(raw[t], max_len)) : 0;
-    B.L[t] = L;
-    B.u[t] = (L + (1 << a_shift) - 1) >> a_shift;
-    short_seq |= in & (L != max_len);
+    B.L[t] = 0;
+    B.u[t] = 0;
+    if (t < B.rows) {  // rows past the first only wait for their own loads when they exist
+      const bool in = t * 64 + lane < n;
+      const int L = in ? max(0, min(raw[t], max_len)) : 0;
+      B.L[t] = L;
+      B.u[t] = (L + (1 << a_shift) - 1) >> a_shift;
+      short_seq |= in & (L != max_len);
+    }
   }
   B.full = __ballot(short_seq) == 0;
   return B;
@@ -698,41 +707,80 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* lse_base, const 
   const int row = blockIdx.x;
   const int b = row / hq;
   const int h = row - b * hq;
-  int raw[kBalancePer];
-  if (p.lens) balance_load(raw, p.lens, p.n, lane);
   const float4* po = reinterpret_cast<const float4*>(p.o) + lane;
 
-  float4 v[kChunk];
-  float l;
-  // Chunk indices j0 .. j0+count-1 (count <= kChunk) into v (and this lane's
-  // lse into l, -inf past count).
-  auto load_chunk = [&](int j0, int count) {
+  // Chunk indices j0 .. j0+count-1 (1 <= count <= kChunk) into vv, and this
+  // lane's lse into lv (-inf past count).  BF (branch-free): entries past
+  // count re-read the last slot and are never used (their weight is 0), so
+  // a wait for loads issued before these does not wait for them too.
+  auto load_chunk = [&](float4 (&vv)[kChunk], float& lv, int j0, int count, auto bf) {
+    constexpr bool BF = decltype(bf)::value;
     int q = j0 / S, r = j0 - q * S;
     if (r + count <= S) {  // one run of consecutive slots
       const int64_t base = (static_cast<int64_t>(q) * hq + h) * S + r;
 #pragma unroll
-      for (int u = 0; u < kChunk; ++u)
-        v[u] = u < count ? po[(base + u) * (kHeadDim / 4)] : make_float4(0.f, 0.f, 0.f, 0.f);
-      l = lane < count ? p.lse[base + lane] : -__builtin_huge_valf();
+      for (int u = 0; u < kChunk; ++u) {
+        if (BF) vv[u] = po[(base + min(u, count - 1)) * (kHeadDim / 4)];
+        else if (u < count) vv[u] = po[(base + u) * (kHeadDim / 4)];
+      }
+      const float x = p.lse[base + min(lane, count - 1)];
+      lv = lane < count ? x : -__builtin_huge_valf();
     } else {
+      int64_t slot = 0;
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
-        const int64_t slot = (static_cast<int64_t>(q) * hq + h) * S + r;
-        v[u] = u < count ? po[slot * (kHeadDim / 4)] : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (u < count) slot = (static_cast<int64_t>(q) * hq + h) * S + r;
+        if (BF || u < count) vv[u] = po[slot * (kHeadDim / 4)];
         if (++r == S) {
           r = 0;
           ++q;
         }
       }
-      const int jl = j0 + lane;
+      const int jl = j0 + min(lane, count - 1);
       const int ql = jl / S;
-      l = lane < count ? p.lse[(static_cast<int64_t>(ql) * hq + h) * S + (jl - ql * S)]
-                       : -__builtin_huge_valf();
+      const float x = p.lse[(static_cast<int64_t>(ql) * hq + h) * S + (jl - ql * S)];
+      lv = lane < count ? x : -__builtin_huge_valf();
     }
   };
 
+  float M = -__builtin_huge_valf(), den = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  // Online log-sum-exp merge of one chunk into (M, den, acc).
+  auto combine = [&](const float4 (&vv)[kChunk], float lv) {
+    float mc = lv;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mc = fmaxf(mc, __shfl_xor(mc, o));
+    const float m_new = fmaxf(M, mc);
+    if (m_new == -__builtin_huge_valf()) return;  // nothing live so far
+    const float alpha = __builtin_amdgcn_exp2f(M - m_new);  // 0 when M = -inf
+    const float wl = lv == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(lv - m_new);
+    float ws = wl;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
+    den = den * alpha + ws;
+    acc.x *= alpha;
+    acc.y *= alpha;
+    acc.z *= alpha;
+    acc.w *= alpha;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
+      if (w != 0.f) {
+        acc.x += w * vv[u].x;
+        acc.y += w * vv[u].y;
+        acc.z += w * vv[u].z;
+        acc.w += w * vv[u].w;
+      }
+    }
+    M = m_new;
+  };
+
+  int raw[kBalancePer];
+  if (p.lens) balance_load(raw, p.lens, p.n, lane);
   int start = b * S, cnt = S;
-  load_chunk(start, min(cnt, kChunk));
+  float4 v[kChunk];
+  float l;
+  load_chunk(v, l, start, min(cnt, kChunk), std::true_type{});
   bool reload = false;
   if (p.lens) {
     const Balance B = balance_finish(raw, p.n, p.max_len, p.a_shift, lane);
@@ -747,36 +795,16 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* lse_base, const 
     }
   }
 
-  float M = -__builtin_huge_valf(), den = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = 0; c0 < cnt; c0 += kChunk) {
-    if (c0 > 0 || reload) load_chunk(start + c0, min(cnt - c0, kChunk));
-    float mc = l;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mc = fmaxf(mc, __shfl_xor(mc, o));
-    const float m_new = fmaxf(M, mc);
-    if (m_new == -__builtin_huge_valf()) continue;  // nothing live so far
-    const float alpha = __builtin_amdgcn_exp2f(M - m_new);  // 0 when M = -inf
-    const float wl = l == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(l - m_new);
-    float ws = wl;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
-    den = den * alpha + ws;
-    acc.x *= alpha;
-    acc.y *= alpha;
-    acc.z *= alpha;
-    acc.w *= alpha;
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
-      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
-      if (w != 0.f) {
-        acc.x += w * v[u].x;
-        acc.y += w * v[u].y;
-        acc.z += w * v[u].z;
-        acc.w += w * v[u].w;
-      }
-    }
-    M = m_new;
+  int c0 = 0;
+  if (!reload) {  // the first chunk is the one already loaded
+    if (cnt > 0) combine(v, l);
+    c0 = kChunk;
+  }
+  for (; c0 < cnt; c0 += kChunk) {
+    float4 w4[kChunk];
+    float lw;
+    load_chunk(w4, lw, start + c0, min(cnt - c0, kChunk), std::false_type{});
+    combine(w4, lw);
   }
   const float scale = den > 0.f ? 1.f / den : 0.f;
   uint16_t* op = p.out + static_cast<int64_t>(row) * kHeadDim + 4 * lane;
