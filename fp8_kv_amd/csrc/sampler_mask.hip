@@ -27,8 +27,9 @@
 //      list head, sorted in registers; a tournament over the list heads when
 //      there are too many); then the softmax masses in fp32 (exp2 with
 //      log2(e) folded in), a wave prefix sum, and the cut.
-//   3. apply_kernel: out = logit where its value >= cut, else -inf (rows that
-//      are invalid are copied).
+//   3. apply_kernel: -inf over the row, then the kept tokens' logits
+//      scattered back (a token's key gives back its fp32 bits exactly), so
+//      the logits are not read again; rows that are invalid are copied.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -330,6 +331,19 @@ __global__ __launch_bounds__(64) void cut_kernel(MaskParams p) {
   __shared__ uint64_t top[64 * kWaveSortE];
   const int row = blockIdx.x;
   const int lane = threadIdx.x;
+  // The chunk lists of the row, rank-major (list j's rank r at r * n_chunks
+  // + j): the first kSpec ranks of every list are one flat coalesced read,
+  // issued before k is known; ranks at or past k hold stale data and are
+  // zeroed once it is.  Deeper ranks are read only if a list needs them.
+  constexpr int kSpec = 8;
+  const uint64_t* src = p.cand + static_cast<int64_t>(row) * p.n_chunks * p.k_max;
+  const int32_t spec_total = min(kSpec, p.k_max) * p.n_chunks;  // <= 64 kSpec
+  uint64_t sv[kSpec];
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u) {
+    const int32_t e = 64 * u + lane;
+    sv[u] = e < spec_total ? src[e] : 0;
+  }
   int32_t k;
   float pp;
   if (!row_valid(p, row, k, pp)) {
@@ -341,25 +355,33 @@ __global__ __launch_bounds__(64) void cut_kernel(MaskParams p) {
     return;
   }
   const int32_t n = min(k, p.vocab);
-  // The chunk lists of the row (list j at lists + j * k), loaded together.
-  // The first k ranks of every chunk list are contiguous (rank-major): one
-  // flat coalesced read, 16 loads per lane in flight.
-  const uint64_t* src = p.cand + static_cast<int64_t>(row) * p.n_chunks * p.k_max;
   const int32_t total = k * p.n_chunks;
-  constexpr int kBatch = 16;
-  for (int32_t e0 = 0; e0 < total; e0 += 64 * kBatch) {
-    uint64_t v[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int32_t e = e0 + 64 * u + lane;
-      v[u] = e < total ? src[e] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int32_t e = e0 + 64 * u + lane;
-      if (e < total) lists[e] = v[u];
-    }
+  for (int u = 0; u < kSpec; ++u) {
+    const int32_t e = 64 * u + lane;
+    if (e < spec_total) lists[e] = e < total ? sv[u] : 0;
   }
+  // Ranks kSpec .. k-1 of every list (one flat read).
+  int32_t loaded = min(spec_total, total);
+  auto load_rest = [&]() {
+    constexpr int kBatch = 16;
+    for (int32_t e0 = loaded; e0 < total; e0 += 64 * kBatch) {
+      uint64_t v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int32_t e = e0 + 64 * u + lane;
+        v[u] = e < total ? src[e] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int32_t e = e0 + 64 * u + lane;
+        if (e < total) lists[e] = v[u];
+      }
+    }
+    loaded = total;
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
@@ -372,9 +394,17 @@ __global__ __launch_bounds__(64) void cut_kernel(MaskParams p) {
   const uint64_t head = lane < p.n_chunks ? lists[lane] : 0;
   uint32_t T = 0;
   if (n <= p.n_chunks) T = wave_mth_largest(static_cast<uint32_t>(head >> 32), n);
+  // c = list j's entries with keys >= T (lane j), first within the ranks
+  // already loaded; a list that fills them continues after the rest is read.
+  const int32_t lim = loaded / p.n_chunks;
   int32_t c = 0;
   if (lane < p.n_chunks)
-    while (c < k && static_cast<uint32_t>(lists[c * p.n_chunks + lane] >> 32) >= T) ++c;
+    while (c < lim && static_cast<uint32_t>(lists[c * p.n_chunks + lane] >> 32) >= T) ++c;
+  if (__ballot(lane < p.n_chunks && c == lim && lim < k) != 0) {
+    load_rest();
+    if (lane < p.n_chunks && c == lim)
+      while (c < k && static_cast<uint32_t>(lists[c * p.n_chunks + lane] >> 32) >= T) ++c;
+  }
   const uint32_t cincl = wave_incl_scan(static_cast<uint32_t>(c));
   const uint32_t total_c = __builtin_amdgcn_readlane(cincl, 63);
   if (total_c <= 64 * kWaveSortE) {
@@ -391,6 +421,7 @@ __global__ __launch_bounds__(64) void cut_kernel(MaskParams p) {
     else
       sort_top<8>(top, total_c);
   } else {
+    if (loaded < total) load_rest();
     int32_t at = 0;
     uint64_t h = head;
     for (int32_t s = 0; s < n; ++s) {
@@ -438,54 +469,66 @@ __global__ __launch_bounds__(64) void cut_kernel(MaskParams p) {
   // Kept tokens form a prefix of the order: the count is the largest keep.
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) keep = max(keep, __shfl_xor(keep, o));
+  // The kept tokens (a prefix of the order) for the masked write.
+  for (int32_t i = lane; i < keep; i += 64) p.kept[static_cast<int64_t>(row) * p.k_max + i] = top[i];
   if (lane == 0) {
-    p.cut[row] = top[keep - 1];
+    p.cut[row] = static_cast<uint64_t>(keep);
     if (p.status) p.status[row] = 0;
   }
 }
 
-__device__ __forceinline__ float masked(float z, int32_t t, uint64_t cut) {
-  return (cut == 0 || token(key_of(z), t) >= cut) ? z : -__builtin_huge_valf();
-}
-
-// out = logit where its token value is at or above the row's cut, else -inf;
-// cut 0 copies the row.  VEC: rows 16-byte aligned (strides multiples of 4).
+// One workgroup per (row, 4096 logits).  A valid row: -inf over the range,
+// then each kept token inside it written back (at most k_max <= 256 kept
+// tokens, one per thread); the barrier orders the two stores of a kept
+// position.  An invalid row (count 0) is copied.  Unless the call is in
+// place, the fill is issued before the count arrives; an invalid row's copy
+// then rewrites exactly the positions each thread filled, so program order
+// puts the copy last.  VEC: rows 16-byte aligned (strides multiples of 4).
 template <bool VEC>
 __global__ __launch_bounds__(256) void apply_kernel(MaskParams p) {
   const int row = blockIdx.y;
+  const int32_t base = blockIdx.x * (256 * 16);
+  const int32_t end = min(base + 256 * 16, p.vocab);
   const float* src = p.logits + static_cast<int64_t>(row) * p.row_stride;
   float* dst = p.out + static_cast<int64_t>(row) * p.out_stride;
-  if constexpr (VEC) {
-    const int32_t base = blockIdx.x * (256 * 16);
-    float4 zz[4];
+  const bool in_place = src == dst;
+  const uint64_t nk = p.cut[row];
+  uint64_t tok = 0;
+  if (threadIdx.x < nk) tok = p.kept[static_cast<int64_t>(row) * p.k_max + threadIdx.x];
+  const float ninf = -__builtin_huge_valf();
+  // fill(true) writes -inf, fill(false) copies the row; both touch the same
+  // positions from the same thread.
+  auto fill = [&](bool minus_inf) {
+    if constexpr (VEC) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int32_t t = base + 4 * (256 * i + static_cast<int32_t>(threadIdx.x));
-      if (t + 4 <= p.vocab) zz[i] = *reinterpret_cast<const float4*>(src + t);
-    }
-    const uint64_t cut = p.cut[row];  // loaded after the logits: they do not wait for it
+      for (int i = 0; i < 4; ++i) {
+        const int32_t t = base + 4 * (256 * i + static_cast<int32_t>(threadIdx.x));
+        if (t + 4 <= end) {
+          *reinterpret_cast<float4*>(dst + t) =
+              minus_inf ? make_float4(ninf, ninf, ninf, ninf)
+                        : *reinterpret_cast<const float4*>(src + t);
+        } else {
+          for (int32_t u = t; u < end; ++u) dst[u] = minus_inf ? ninf : src[u];
+        }
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int32_t t = base + 4 * (256 * i + static_cast<int32_t>(threadIdx.x));
-      if (t + 4 <= p.vocab) {
-        float4 z = zz[i];
-        z.x = masked(z.x, t, cut);
-        z.y = masked(z.y, t + 1, cut);
-        z.z = masked(z.z, t + 2, cut);
-        z.w = masked(z.w, t + 3, cut);
-        *reinterpret_cast<float4*>(dst + t) = z;
-      } else {
-        for (int32_t u = t; u < p.vocab; ++u) dst[u] = masked(src[u], u, cut);
+      for (int i = 0; i < 16; ++i) {
+        const int32_t t = base + 256 * i + static_cast<int32_t>(threadIdx.x);
+        if (t < end) dst[t] = minus_inf ? ninf : src[t];
       }
     }
-  } else {
-    const uint64_t cut = p.cut[row];
-    const int32_t base = blockIdx.x * (256 * 16);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int32_t t = base + 256 * i + static_cast<int32_t>(threadIdx.x);
-      if (t < p.vocab) dst[t] = masked(src[t], t, cut);
-    }
+  };
+  if (!in_place) fill(true);
+  if (nk == 0) {
+    if (!in_place) fill(false);  // in place, the row already is its own copy
+    return;
+  }
+  if (in_place) fill(true);
+  __syncthreads();
+  if (threadIdx.x < nk) {
+    const int32_t t = static_cast<int32_t>(~static_cast<uint32_t>(tok));
+    if (t >= base && t < end) dst[t] = value_of(static_cast<uint32_t>(tok >> 32));
   }
 }
 
@@ -508,7 +551,7 @@ size_t workspace_bytes(int32_t rows, int32_t vocab, int32_t k_max) {
   int32_t chunk = 0, n_chunks = 0;
   plan_chunks(vocab, &chunk, &n_chunks);
   const size_t cand = sizeof(uint64_t) * static_cast<size_t>(rows) * n_chunks * k_max;
-  return cand + sizeof(uint64_t) * static_cast<size_t>(rows);
+  return cand + sizeof(uint64_t) * static_cast<size_t>(rows) * (1 + k_max);
 }
 
 hipError_t launch_mask(const MaskParams& p, hipStream_t stream) {
