@@ -28,12 +28,12 @@
 //   3. Pivot P, the k-th largest key: MSB-first 8-bit histogram passes over
 //      the candidates with key >= T, skipping the leading bytes that T and the
 //      row's largest key share (all such candidates share them).  Every wave
-//      scans the 256 bins itself, so a pass costs one barrier; three
-//      histogram buffers rotate.  `need` is how many keys equal to P are
-//      kept, `eq` how many there are.  The first pass checks that at least k
-//      candidates reach T and that no region overflowed; otherwise
-//      (adversarial inputs) four exact passes run over the whole row, re-read
-//      from cache.
+//      adds its own region to the shared bins and scans the 256 bins itself,
+//      so a pass costs one barrier; three histogram buffers rotate.  `need`
+//      is how many keys equal to P are kept, `eq` how many there are.  The
+//      first pass checks that at least k candidates reach T and that no
+//      region overflowed; otherwise (adversarial inputs) four exact passes
+//      run over the whole row, re-read from cache.
 //   4. Kept blocks (key > P, or key >= P when every tie is kept) are marked in
 //      an LDS bitmap from the candidates; when eq > need the tied blocks go to
 //      a second bitmap of which a block-wide popcount scan keeps the first
@@ -70,9 +70,7 @@ struct TopkShared {
   uint32_t twave[kWaves];
   uint32_t tmax[kWaves];
   uint32_t wsum[2][kWaves];
-  uint32_t gather[64];        // keys of the pivot's bin once it holds <= 64
   uint32_t wcnt[kWaves];      // candidates per wave region
-  uint32_t result[4];         // pivot key, need, eq, ok (from wave 0)
 };
 
 __device__ __forceinline__ uint32_t key_of_bits(uint32_t u) {
@@ -132,24 +130,6 @@ __device__ __forceinline__ uint32_t wave_mth_largest(uint32_t x, uint32_t m) {
   for (int b = 31; b >= 0; --b) {
     const uint32_t trial = res | (1u << b);
     const uint32_t c = static_cast<uint32_t>(__popcll(__ballot((x >> b) == (trial >> b))));
-    if (c >= m)
-      res = trial;
-    else
-      m -= c;
-  }
-  return res;
-}
-
-// The m-th largest (1 <= m <= number of active lanes) of the active lanes'
-// values, all of which equal `prefix` above bit `bits`: bisection over the
-// low bits.
-__device__ __forceinline__ uint32_t wave_mth_largest_low(uint32_t x, bool act, uint32_t m,
-                                                         uint32_t prefix, int bits) {
-  uint32_t res = prefix;
-  for (int b = bits - 1; b >= 0; --b) {
-    const uint32_t trial = res | (1u << b);
-    const uint32_t c =
-        static_cast<uint32_t>(__popcll(__ballot(act && (x >> b) == (trial >> b))));
     if (c >= m)
       res = trial;
     else
@@ -245,62 +225,37 @@ __device__ __forceinline__ Pivot pivot_block(TopkShared& sh, uint32_t k, Visit v
   return pv;
 }
 
-// Orders this wave's LDS accesses: earlier ones complete before later ones
-// start (a single wave needs no barrier for its own LDS traffic).
-__device__ __forceinline__ void lds_fence_wave() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// Single-wave pivot search over the per-wave candidate regions (keys >= T
-// count; all of them share the top `first` bytes of T).  MSB-first 8-bit
-// passes with the histogram in sh.hist[0]; once the pivot's bin holds at most
-// 64 keys they are gathered into lanes and a ballot bisection over the
-// remaining low bits finishes.  ok is false if a region overflowed or fewer
-// than k keys reach T.
-__device__ __forceinline__ Pivot pivot_wave(TopkShared& sh, uint32_t k, uint32_t T, int first) {
+// Block-wide pivot search over the per-wave candidate regions (keys >= T
+// count; all of them share the top `first` bytes of T): every wave
+// histograms its own region into the shared bins, one barrier per 8-bit
+// pass, and every wave finds the digit itself.  Three histogram buffers
+// rotate (all three zeroed before the first barrier of the call).  ok is
+// false, for every wave alike, if a region overflowed or fewer than k keys
+// reach T.
+__device__ __forceinline__ Pivot pivot_regions(TopkShared& sh, uint32_t k, uint32_t T, int first,
+                                               const uint2* region, uint32_t used) {
   const int lane = lane_id();
-  Pivot pv{0, 0, 0, true};
-  uint32_t n[kWaves];
   bool overflow = false;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    n[w] = __builtin_amdgcn_readfirstlane(sh.wcnt[w]);
-    overflow |= n[w] > static_cast<uint32_t>(kRegion);
-    n[w] = n[w] < static_cast<uint32_t>(kRegion) ? n[w] : kRegion;
-  }
-  // Visit every candidate key >= T: first chunk of each region unrolled so its
-  // reads are in flight together, the rest (regions over 64) in a loop.
-  auto visit = [&](auto f) {
-    uint32_t kx[kWaves];
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      kx[w] = static_cast<uint32_t>(lane) < n[w] ? sh.cand[kRegion * w + lane].x : 0u;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const uint32_t key = key_of_bits(kx[w]);
-      f(static_cast<uint32_t>(lane) < n[w] && key >= T, key);
-    }
-    for (int w = 0; w < kWaves; ++w)
-      for (uint32_t b = 64; b < n[w]; b += 64) {
-        const uint32_t e = b + lane;
-        const uint32_t key = key_of_bits(e < n[w] ? sh.cand[kRegion * w + e].x : 0u);
-        f(e < n[w] && key >= T, key);
-      }
-  };
+  for (int w = 0; w < kWaves; ++w) overflow |= sh.wcnt[w] > static_cast<uint32_t>(kRegion);
+  Pivot pv{0, 0, 0, true};
   uint32_t prefix = first == 0 ? 0u : (T & (0xFFFFFFFFu << (32 - 8 * first)));
   uint32_t rem = k;
-  uint32_t* hist = sh.hist[0];
   for (int q = first; q < 4; ++q) {
     const int shift = 24 - 8 * q;
     const uint32_t hi_mask = q == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-#pragma unroll
-    for (int m = 0; m < 4; ++m) hist[4 * lane + m] = 0;
-    lds_fence_wave();
-    visit([&](bool act, uint32_t key) {
-      if (act && ((key ^ prefix) & hi_mask) == 0) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    });
-    lds_fence_wave();
+    uint32_t* hist = sh.hist[q % 3];
+    for (uint32_t b = 0; b < used; b += 64) {
+      const uint32_t e = b + lane;
+      const uint32_t key = key_of_bits(e < used ? region[e].x : 0u);
+      if (e < used && key >= T && ((key ^ prefix) & hi_mask) == 0)
+        atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // Zero the buffer of pass q + 2: every wave finished reading it (pass
+    // q - 1) before this barrier, and pass q + 2 adds to it only after the
+    // next one.
+    if (threadIdx.x < 256) sh.hist[(q + 2) % 3][threadIdx.x] = 0;
     const Digit d = find_digit(hist, rem);
     if (q == first && (d.total < k || overflow)) {
       pv.ok = false;
@@ -309,26 +264,6 @@ __device__ __forceinline__ Pivot pivot_wave(TopkShared& sh, uint32_t k, uint32_t
     prefix |= d.digit << shift;
     rem -= d.above;
     pv.eq = d.in_bin;
-    if (shift > 0 && d.in_bin <= 64) {
-      // Gather the pivot's bin into lanes and bisect its low `shift` bits.
-      const uint32_t lo_mask = 0xFFFFFFFFu << shift;
-      uint32_t got = 0;
-      visit([&](bool act, uint32_t key) {
-        const bool in = act && ((key ^ prefix) & lo_mask) == 0;
-        const uint64_t m = __ballot(in);
-        const uint32_t at = got + lanes_below(m);
-        if (in && at < 64) sh.gather[at] = key;
-        got += static_cast<uint32_t>(__popcll(m));
-      });
-      lds_fence_wave();
-      const bool act = static_cast<uint32_t>(lane) < d.in_bin;
-      const uint32_t key = act ? sh.gather[lane] : 0u;
-      const uint32_t P = wave_mth_largest_low(key, act, rem, prefix, shift);
-      pv.key = P;
-      pv.eq = static_cast<uint32_t>(__popcll(__ballot(act && key == P)));
-      pv.need = rem - static_cast<uint32_t>(__popcll(__ballot(act && key > P)));
-      return pv;
-    }
   }
   pv.key = prefix;
   pv.need = rem;
@@ -404,6 +339,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   if (tid < 256) {
     sh.hist[0][tid] = 0;
     sh.hist[1][tid] = 0;
+    sh.hist[2][tid] = 0;
   }
   sh.keep[2 * tid] = 0;
   sh.keep[2 * tid + 1] = 0;
@@ -485,32 +421,21 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   const uint2* region = sh.cand + kRegion * wave;
   __syncthreads();
 
-  // ---- 3. the pivot over the candidates with key >= T (wave 0).  Candidates
-  // with key in [T, top] share the leading bytes of T and top.
+  // ---- 3. the pivot over the candidates with key >= T (all waves, each
+  // over its own region).  Candidates with key in [T, top] share the leading
+  // bytes of T and top.
   const uint32_t kk = static_cast<uint32_t>(k);
-  if (wave == 0) {
-    int first = 0;
-    if (float_cand) {
-      const uint32_t diff = T ^ top;
-      first = diff == 0 ? 3 : (__clz(diff) >> 3);
-    }
-    const Pivot w = pivot_wave(sh, kk, T, first);
-    if (lane == 0) {
-      sh.result[0] = w.key;
-      sh.result[1] = w.need;
-      sh.result[2] = w.eq;
-      sh.result[3] = w.ok ? 1u : 0u;
-    }
+  int first = 0;
+  if (float_cand) {
+    const uint32_t diff = T ^ top;
+    first = diff == 0 ? 3 : (__clz(diff) >> 3);
   }
-  __syncthreads();
-  Pivot pv;
-  pv.key = __builtin_amdgcn_readfirstlane(sh.result[0]);
-  pv.need = __builtin_amdgcn_readfirstlane(sh.result[1]);
-  pv.eq = __builtin_amdgcn_readfirstlane(sh.result[2]);
-  const bool fast_pivot = __builtin_amdgcn_readfirstlane(sh.result[3]) != 0;
+  Pivot pv = pivot_regions(sh, kk, T, first, region, used);
+  const bool fast_pivot = pv.ok;
   if (!fast_pivot) {
-    // Exact passes over the whole row, re-read from cache.  sh.hist[0] was
-    // last written by wave 0 before the barrier above.
+    // Exact passes over the whole row, re-read from cache, once every wave
+    // has left the candidate passes.
+    __syncthreads();
     if (tid < 256) {
       sh.hist[0][tid] = 0;
       sh.hist[1][tid] = 0;
