@@ -81,7 +81,7 @@ def cpu_baseline_topk(case, budget_s: float) -> dict:
     (the first rows of the workload, doubling until about `budget_s`)."""
     import oracle
 
-    rows, el = 16, 0.0
+    rows, el = min(16, case.rows), 0.0
     while True:
         t0 = time.perf_counter()
         oracle.topk_select(case.scores[:rows], case.k, case.n_valid[:rows],
@@ -160,7 +160,7 @@ def cpu_baseline_page4(case, budget_s: float) -> dict:
     first rows of the workload, doubling until about `budget_s`)."""
     import oracle
 
-    rows, el = 64, 0.0
+    rows, el = min(64, case.rows), 0.0
     while True:
         t0 = time.perf_counter()
         oracle.qsa_page4_table(case.tokens[:rows], case.live_len[:rows], case.block_table,
