@@ -184,6 +184,22 @@ def test_sparse_prefill_fp8_contiguous(pg):
     _check(pg, case, "prefill fp8 contiguous", prefill=True)
 
 
+def test_sparse_prefill_unequal_rows_balanced(pg):
+    """Rows cut to unequal live lengths (one empty) with several splits: the
+    balanced split plan in prefill mode."""
+    case = inputs.sparse_prefill_case(rows=64, selected_blocks=40, tail=2, pool_blocks=512,
+                                      seed=57)
+    rng = np.random.default_rng(57)
+    lens = case.lens.copy()
+    cut = rng.choice(case.n, 24, replace=False)
+    lens[cut] = rng.integers(1, int(lens.max()), size=cut.size)
+    lens[5] = 0
+    case = dataclasses.replace(case, lens=lens.astype(np.int32))
+    for s in (0, 3):
+        got = _check(pg, case, f"prefill unequal rows splits {s}", prefill=True, num_splits=s)
+        assert np.all(got[5] == 0)
+
+
 # ----------------------------------------------------------- special cases
 def test_length_one_is_v(pg):
     case = inputs.decode_case(batch=4, lens=1, page_size=16, kv_dtype=E4M3, seed=60,
