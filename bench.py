@@ -298,14 +298,17 @@ def bench_sampler(args) -> int:
 
 def time_steps(step, steps: int, warmup: int, R: int, use_graph: bool) -> float:
     """Average milliseconds per step over exactly `steps` steps, timed with HIP
-    events on the stream the kernels run on.  With use_graph the R steps of
-    one pool rotation are captured once into a HIP graph and replayed (plus
-    steps % R eager steps), so Python's per-call overhead cannot leave the GPU
-    idle between steps."""
+    events on the stream the kernels run on.  With use_graph the steps are
+    captured into one HIP graph (up to kGraphSteps of them, cycling through the
+    R pools, replayed as often as needed, the remainder eager), as a serving
+    loop captures a whole decode step, so neither Python's per-call overhead
+    nor graph-launch boundaries leave the GPU idle between steps."""
     import torch
 
+    kGraphSteps = 512
     cur = torch.cuda.current_stream()
-    if use_graph:
+    G = min(steps, kGraphSteps)
+    if use_graph and G > 0:
         side = torch.cuda.Stream()
         side.wait_stream(cur)
         with torch.cuda.stream(side):
@@ -315,21 +318,24 @@ def time_steps(step, steps: int, warmup: int, R: int, use_graph: bool) -> float:
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for i in range(R):
+            for i in range(G):
                 step(i)
-        rotation = graph.replay
+        replay, per_replay = graph.replay, G
     else:
-        def rotation():
+        def replay():
             for i in range(R):
                 step(i)
+        per_replay = R
     for i in range(warmup):
         step(i)
+    if use_graph and G > 0:
+        replay()  # the graph's first launch uploads it: keep that out of the timing
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(cur)
-    for _ in range(steps // R):
-        rotation()
-    for i in range(steps % R):
+    for _ in range(steps // per_replay):
+        replay()
+    for i in range(steps % per_replay):
         step(i)
     e1.record(cur)
     torch.cuda.synchronize()
