@@ -2,8 +2,8 @@
 // launches on the caller's stream.  Declared in include/pgqa.h.
 //
 // Validation runs before any HIP call, so every argument error is reported
-// without touching a device ("fail closed": nothing launched, nothing
-// written).  The only HIP queries are the current device and its compute
+// without touching a device: nothing is launched and nothing is written.
+// The only HIP queries are the current device and its compute
 // unit count (cached per device), needed for the automatic split count.
 #include <hip/hip_runtime.h>
 
