@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -36,11 +37,21 @@ KERNEL_SOURCES = [os.path.join(ROOT, "fp8_kv_amd", "csrc", f)
                   for f in ("pgqa_kernels.hip", "pgqa_api.hip", "pgqa_internal.h")]
 
 
+_C_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\])*"', re.S)
+
+
+def code_of(text: str) -> str:
+    """C/C++ source without comments, whitespace runs collapsed: what the
+    compiler sees, so a comment edit does not count as a kernel change."""
+    text = _C_TOKENS.sub(lambda m: " " if m.group(0).startswith("/") else m.group(0), text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(code_of(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -496,6 +496,8 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   // Partial slot (split partials only): (b, split) here, and in a balanced
   // plan too, where this workgroup's chunk index is J = b*S + split.
   const int slot_row = b, slot_col = split;
+  // Every sequence's length, for the balanced plan: issued first, so that
+  // waiting for them does not also wait for the page-table prefetch.
   int raw[kBalancePer];
   if (bal_n > 0) balance_load(raw, p.lens, bal_n, lane);
 
