@@ -515,7 +515,9 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   // its K/V loads (loads complete in issue order, so waiting for a page id
   // never drains K/V loads issued after it).  The first entries are loaded
   // before the sequence length is known, so they share its memory latency.
-  constexpr int RP = PL + 1;                      // page-entry ring
+  // Page-entry ring: the first PD - 1 + PL entries are loaded before the first
+  // K/V loads are issued, so it holds that many (PL + 1 would do after that).
+  constexpr int RP = PD - 1 + PL;
   constexpr int U = PD * RP / gcd_const(PD, RP);  // unroll: ring indices are constants
   int pg[RP], ps[RP];  // page-table entry and slot-in-page, per ring position
 #pragma unroll
