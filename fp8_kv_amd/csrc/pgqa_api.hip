@@ -35,6 +35,11 @@ constexpr int kChunkAlign = kTile * kWaves;  // split length granularity
 constexpr int kChunkAlignShift = kWaves == 4 ? 6 : 7;
 static_assert(kWaves == 4 || kWaves == 8, "workgroups have 4 or 8 waves");
 static_assert(kChunkAlign == 1 << kChunkAlignShift, "granularity is a power of two");
+// Rows up to this length, when there are enough of them to give every compute
+// unit a workgroup of kWaves rows, run one row per wave.
+#ifndef PGQA_ROW_PER_WAVE_MAX_LEN
+#define PGQA_ROW_PER_WAVE_MAX_LEN 4096
+#endif
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
@@ -203,6 +208,11 @@ int run_attention(const void* q, const pgqa_kv_pool* kv, const int32_t* table, i
     // Unequal lengths: the kernels spread the live tokens over all n*S
     // workgroup slots of a kv head (the partial layout stays internal).
     if (n <= pgqa::kBalanceMaxSeqs) p.balance_n = n;
+  } else if (max_len <= PGQA_ROW_PER_WAVE_MAX_LEN) {
+    // One split and many rows: a workgroup of kWaves rows pays its launch
+    // and ramp once for all of them.
+    const int cus = current_cu_count();
+    p.row_per_wave = cus > 0 && static_cast<int64_t>(n) * hkv >= static_cast<int64_t>(kWaves) * cus;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (pgqa::launch_attention(p, fp8, s) != hipSuccess) return PGQA_ERR_HIP;

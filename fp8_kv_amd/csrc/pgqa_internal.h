@@ -40,6 +40,7 @@ struct AttnParams {
   int32_t balance_n;       // n > 0: spread unequal lengths over the n*splits slots
                            // (split partials only, n <= kBalanceMaxSeqs); 0: static
   bool partials;           // write split partials (ws_o, ws_lse) instead of out
+  bool row_per_wave;       // one split: each wave owns a whole (row, kv head)
   bool stream_kv;          // non-temporal K/V loads (each byte read once per call)
   uint16_t* out;           // fp16 bits [n][hq][256]
   float* ws_o;             // [n*hq][splits][256] split outputs (v_scale applied)

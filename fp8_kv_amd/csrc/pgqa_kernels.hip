@@ -289,8 +289,11 @@ struct TileRegs {
   u4_t v[4][Geo<FP8>::kV];
 };
 
-template <bool FP8, int NW, bool NT>
+// RW (row per wave): the wave walks every tile of its own row; otherwise
+// wave w of NW takes tiles w, w + NW, ... of the workgroup's range.
+template <bool FP8, int NW, bool NT, bool RW>
 struct Wave {
+  static constexpr int kTileStride = RW ? 1 : NW;
   // constant per wave
   const AttnParams& p;
   const int32_t* tab;
@@ -304,7 +307,7 @@ struct Wave {
   bool bad;
 
   __device__ __forceinline__ int tile_start(int k) const {
-    return s0 + (wave + NW * k) * kTile;
+    return s0 + ((RW ? 0 : wave) + kTileStride * k) * kTile;
   }
 
   // q^T operand of sequence b, kv head g: head r of the group (zero past the
@@ -461,7 +464,7 @@ constexpr int gcd_const(int a, int b) { return b == 0 ? a : gcd_const(b, a % b);
 // library is built with kernel-argument preloading, so they arrive in SGPRs at
 // wave launch and those loads do not wait for the parameter block (which is
 // fetched from memory in parallel).
-template <bool FP8, int NW, int PD, int PL, bool NT>
+template <bool FP8, int NW, int PD, int PL, bool NT, bool RW>
 __global__ __launch_bounds__(64 * NW) void attention_kernel(
     const int32_t* table, const int32_t* lens, int32_t max_pages, int32_t max_len, int32_t chunk,
     int32_t splits, int32_t hkv, int32_t page_size, float inv_page_size, int32_t bal_n,
@@ -482,8 +485,11 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   // on scalar branches.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wg = blockIdx.x;
-  const int split = wg % p.splits;
-  const int bg = wg / p.splits;
+  // Row per wave (one split only): wave w of workgroup wg owns (sequence,
+  // kv head) NW * wg + w.
+  const int split = RW ? 0 : wg % p.splits;
+  const int bg = RW ? NW * wg + wave : wg / p.splits;
+  if (RW && bg >= p.n * p.hkv) return;  // past the last row (whole wave)
   int b = bg / p.hkv;
   const int g = bg - b * p.hkv;
 
@@ -501,7 +507,7 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   int raw[kBalancePer];
   if (bal_n > 0) balance_load(raw, p.lens, bal_n, lane);
 
-  Wave<FP8, NW, NT> W{p};
+  Wave<FP8, NW, NT, RW> W{p};
   W.tab = p.table + static_cast<int64_t>(b) * p.max_pages;
   W.head_off = static_cast<int64_t>(g) * p.head_stride;
   W.s0 = s0;
@@ -564,8 +570,9 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
 #pragma unroll
   for (int j = 0; j < 16; ++j) W.acc[j] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int span = s1 - s0 - wave * kTile;
-  const int ntiles = span > 0 ? (span + NW * kTile - 1) / (NW * kTile) : 0;
+  constexpr int kStep = Wave<FP8, NW, NT, RW>::kTileStride * kTile;  // tokens between own tiles
+  const int span = s1 - s0 - (RW ? 0 : wave) * kTile;
+  const int ntiles = span > 0 ? (span + kStep - 1) / kStep : 0;
 
   // The loop body is straight-line so the wait counts are exact; it runs to a
   // multiple of U tiles.  Tiles past the wave's range load only the cached
@@ -586,6 +593,32 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
         if (k + j < ntiles) W.process(R[j % PD], k + j);
       }
     }
+  }
+
+  if constexpr (RW) {
+    // The wave holds its whole row: normalise and store from registers.
+    float l_tot = W.l_run + __shfl_xor(W.l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const bool bad = __ballot(W.bad) != 0;
+    if (W.r < p.group) {
+      // v_scale applied; an empty row (l = 0) gives zeros; a bad page NaNs.
+      const float scale = bad ? __builtin_nanf("") : (l_tot > 0.f ? p.v_scale / l_tot : 0.f);
+      uint16_t* orow =
+          p.out + (static_cast<int64_t>(b) * p.hq + g * p.group + W.r) * kHeadDim;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          u2_t packed;
+          packed[0] = f16_bits(W.acc[4 * jj][i] * scale) |
+                      (static_cast<uint32_t>(f16_bits(W.acc[4 * jj + 1][i] * scale)) << 16);
+          packed[1] = f16_bits(W.acc[4 * jj + 2][i] * scale) |
+                      (static_cast<uint32_t>(f16_bits(W.acc[4 * jj + 3][i] * scale)) << 16);
+          *reinterpret_cast<u2_t*>(orow + W.out_dim(4 * jj, i)) = packed;
+        }
+      }
+    }
+    return;
   }
 
   // ---- merge the waves of the workgroup through LDS
@@ -824,25 +857,32 @@ __global__ void e4m3_table_kernel(float* out) {
   out[c] = static_cast<float>(__builtin_bit_cast(h2_t, h)[0]);
 }
 
-template <bool FP8, int NW, bool NT>
+template <bool FP8, int NW, bool NT, bool RW>
 hipError_t launch(const AttnParams& p, hipStream_t stream) {
   constexpr int PD = PGQA_PIPELINE_DEPTH;
   constexpr int PL = PGQA_PAGE_LOOKAHEAD;
-  const size_t lds = attention_lds_bytes(p.group, NW);
+  const size_t lds = RW ? 0 : attention_lds_bytes(p.group, NW);
   if (lds > 65536) {
     // Merge buffers beyond the default 64 KiB dynamic LDS limit need the
     // limit raised (once per process and kernel).
     static const hipError_t raised = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(attention_kernel<FP8, NW, PD, PL, NT>),
+        reinterpret_cast<const void*>(attention_kernel<FP8, NW, PD, PL, NT, RW>),
         hipFuncAttributeMaxDynamicSharedMemorySize,
         static_cast<int>(attention_lds_bytes(kMaxGroup, NW)));
     if (raised != hipSuccess) return raised;
   }
-  const dim3 grid(static_cast<unsigned>(p.splits) * p.n * p.hkv);
-  hipLaunchKernelGGL((attention_kernel<FP8, NW, PD, PL, NT>), grid, dim3(64 * NW), lds, stream,
+  const int64_t rows = static_cast<int64_t>(p.n) * p.hkv;
+  const dim3 grid(static_cast<unsigned>(RW ? (rows + NW - 1) / NW : p.splits * rows));
+  hipLaunchKernelGGL((attention_kernel<FP8, NW, PD, PL, NT, RW>), grid, dim3(64 * NW), lds, stream,
                      p.table, p.lens, p.max_pages, p.max_len, p.chunk, p.splits, p.hkv,
                      p.page_size, p.inv_page_size, p.balance_n, p);
   return hipGetLastError();
+}
+
+template <bool FP8, int NW, bool NT>
+hipError_t launch_rw(const AttnParams& p, hipStream_t stream) {
+  return p.row_per_wave ? launch<FP8, NW, NT, true>(p, stream)
+                        : launch<FP8, NW, NT, false>(p, stream);
 }
 
 }  // namespace
@@ -855,14 +895,14 @@ size_t attention_lds_bytes(int group, int waves) {
 hipError_t launch_attention(const AttnParams& p, bool fp8, hipStream_t stream) {
   if (p.stream_kv) {
     switch (p.waves) {
-      case 4: return fp8 ? launch<true, 4, true>(p, stream) : launch<false, 4, true>(p, stream);
-      case 8: return fp8 ? launch<true, 8, true>(p, stream) : launch<false, 8, true>(p, stream);
+      case 4: return fp8 ? launch_rw<true, 4, true>(p, stream) : launch_rw<false, 4, true>(p, stream);
+      case 8: return fp8 ? launch_rw<true, 8, true>(p, stream) : launch_rw<false, 8, true>(p, stream);
       default: return hipErrorInvalidValue;
     }
   }
   switch (p.waves) {
-    case 4: return fp8 ? launch<true, 4, false>(p, stream) : launch<false, 4, false>(p, stream);
-    case 8: return fp8 ? launch<true, 8, false>(p, stream) : launch<false, 8, false>(p, stream);
+    case 4: return fp8 ? launch_rw<true, 4, false>(p, stream) : launch_rw<false, 4, false>(p, stream);
+    case 8: return fp8 ? launch_rw<true, 8, false>(p, stream) : launch_rw<false, 8, false>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

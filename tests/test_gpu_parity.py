@@ -200,6 +200,42 @@ def test_sparse_prefill_unequal_rows_balanced(pg):
         assert np.all(got[5] == 0)
 
 
+# ------------------------------------------- one row per wave (many rows)
+@pytest.mark.parametrize("kv_dtype,layout", [(E4M3, "contiguous"), (FP16, "interleaved")])
+def test_row_per_wave_many_short_rows(pg, kv_dtype, layout):
+    """1100 sequences with one split: each wave owns a whole sequence (ragged
+    lengths from empty to several hundred tokens, one bad page id).  Unit
+    scales: rows of a few tokens output values of V itself, and above 4 in
+    magnitude half an fp16 ULP alone exceeds the 2e-3 bar."""
+    rng = np.random.default_rng(101)
+    lens = rng.integers(-2, 300, size=1100)
+    lens[:3] = [0, 1, 299]
+    case = inputs.decode_case(batch=1100, lens=lens, page_size=16, kv_dtype=kv_dtype,
+                              layout=layout, seed=101, scales="unit", max_seq_len=300)
+    t = case.table.copy()
+    t[7, 0] = case.num_pages + 1                      # row 7 reads a bad page
+    bad = dataclasses.replace(case, table=t)
+    got = _run(pg, bad, num_splits=1)
+    assert np.isnan(got[7]).all() if lens[7] > 0 else np.all(got[7] == 0)
+    ids = np.array([i for i in range(case.n) if i != 7], dtype=np.int32)
+    ref = oracle.paged_gqa(**case.oracle_kwargs(), seq_ids=ids)
+    assert_parity(got[ids], ref, f"row per wave {kv_dtype} {layout}")
+    assert np.all(got[lens <= 0] == 0)
+
+
+def test_row_per_wave_multi_kv_head_and_prefill(pg):
+    """Rows x kv heads = 1200 (Hkv = 2), and a 1024-row sparse prefill: the
+    row-per-wave kernel against the oracle and, bitwise, prefill = decode."""
+    case = inputs.decode_case(batch=600, lens=("uniform", 1, 200), page_size=32, kv_dtype=E4M3,
+                              num_q_heads=12, num_kv_heads=2, seed=102, scales="uniform")
+    _check(pg, case, "row per wave hkv2", num_splits=1)
+    case = inputs.sparse_prefill_case(rows=1024, selected_blocks=16, tail=3, pool_blocks=1400,
+                                      seed=103)
+    a = _check(pg, case, "row per wave prefill", prefill=True)
+    b = _run(pg, case, prefill=False)
+    assert np.array_equal(a, b)
+
+
 # ----------------------------------------------------------- special cases
 def test_length_one_is_v(pg):
     case = inputs.decode_case(batch=4, lens=1, page_size=16, kv_dtype=E4M3, seed=60,
