@@ -40,7 +40,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kPerThread = kMaxChunk / kThreads;  // 32
 
 __device__ __forceinline__ uint32_t key_of(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -176,6 +175,9 @@ __device__ __forceinline__ void sort_and_write(const uint64_t* cand, uint32_t n_
   for (int32_t i = 64 * E + lane; i < k; i += 64) dst[static_cast<int64_t>(i) * n_chunks] = 0;
 }
 
+// PER entries per thread: chunks of up to 256 PER logits (16 for the usual
+// 4096, 32 for the largest); the work per thread scales with PER.
+template <int PER>
 __global__ __launch_bounds__(kThreads) void chunk_top_kernel(MaskParams p) {
   extern __shared__ uint64_t cand[];  // [pow2 >= chunk] candidates, then padding
   __shared__ uint32_t wval[kWaves];
@@ -191,9 +193,9 @@ __global__ __launch_bounds__(kThreads) void chunk_top_kernel(MaskParams p) {
   // Thread t holds entries t + 256 i; key 0 (never a logit's key but the
   // negative NaN 0xFFFFFFFF's) marks entries past the chunk.  The loads are
   // issued before the row's k and p are known.
-  uint32_t key[kPerThread];
+  uint32_t key[PER];
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const int32_t e = tid + kThreads * i;
     key[i] = e < len ? __float_as_uint(src[e]) : 0xFFFFFFFFu;
   }
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void chunk_top_kernel(MaskParams p) {
   const int32_t kc = min(k, len);
   uint32_t lmax = 0;
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
+  for (int i = 0; i < PER; ++i) {
     key[i] = key_of(__uint_as_float(key[i]));  // 0xFFFFFFFF (past the chunk) -> key 0
     lmax = max(lmax, key[i]);
   }
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void chunk_top_kernel(MaskParams p) {
   // Candidates (entries with key >= T) to LDS, compacted in thread order.
   uint32_t cnt = 0;
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) cnt += (tid + kThreads * i < len && key[i] >= T) ? 1u : 0u;
+  for (int i = 0; i < PER; ++i) cnt += (tid + kThreads * i < len && key[i] >= T) ? 1u : 0u;
   const uint32_t incl = wave_incl_scan(cnt);
   if (lane == 63) wval[wave] = incl;
   __syncthreads();
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void chunk_top_kernel(MaskParams p) {
     n_c += wval[w];
   }
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const int32_t e = tid + kThreads * i;
     if (e < len && key[i] >= T) cand[pos++] = token(key[i], start + e);
   }
@@ -561,14 +563,20 @@ hipError_t launch_mask(const MaskParams& p, hipStream_t stream) {
   size_t pow2 = 64;
   while (pow2 < static_cast<size_t>(p.chunk)) pow2 <<= 1;
   const size_t lds1 = sizeof(uint64_t) * pow2;
-  if (lds1 > 65536 - 64) {
-    static const hipError_t raised = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(chunk_top_kernel),
-        hipFuncAttributeMaxDynamicSharedMemorySize,
-        static_cast<int>(sizeof(uint64_t) * kMaxChunk));
-    if (raised != hipSuccess) return raised;
+  const dim3 grid1(p.n_chunks, p.rows);
+  if (p.chunk <= 16 * kThreads) {
+    hipLaunchKernelGGL(chunk_top_kernel<16>, grid1, dim3(kThreads), lds1, stream, p);
+  } else {
+    if (lds1 > 65536 - 64) {
+      static const hipError_t raised = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(chunk_top_kernel<kMaxChunk / kThreads>),
+          hipFuncAttributeMaxDynamicSharedMemorySize,
+          static_cast<int>(sizeof(uint64_t) * kMaxChunk));
+      if (raised != hipSuccess) return raised;
+    }
+    hipLaunchKernelGGL(chunk_top_kernel<kMaxChunk / kThreads>, grid1, dim3(kThreads), lds1, stream,
+                       p);
   }
-  hipLaunchKernelGGL(chunk_top_kernel, dim3(p.n_chunks, p.rows), dim3(kThreads), lds1, stream, p);
   const size_t lds = sizeof(uint64_t) * static_cast<size_t>(p.n_chunks) * p.k_max;
   if (lds > 65536) {
     static const hipError_t raised = hipFuncSetAttribute(
