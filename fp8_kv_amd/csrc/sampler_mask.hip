@@ -60,7 +60,7 @@ __device__ __forceinline__ bool row_valid(const MaskParams& p, int row, int32_t&
 
 // The m-th largest (1 <= m <= 64) of the wave's 64 lane values, by bisection
 // on the bits from the top.
-__device__ __forceinline__ uint32_t wave_mth_largest(uint32_t x, uint32_t m) {
+__device__ __forceinline__ uint32_t wave_mth_largest_bits(uint32_t x, uint32_t m) {
   uint32_t res = 0;
 #pragma unroll
   for (int b = 31; b >= 0; --b) {
@@ -74,13 +74,50 @@ __device__ __forceinline__ uint32_t wave_mth_largest(uint32_t x, uint32_t m) {
   return res;
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = static_cast<uint32_t>(__shfl_up(static_cast<int>(x), d));
-    if (lane >= d) x += y;
+// x combined with the lane the DPP control CTRL names, in the rows ROWS
+// enables (lanes without a source see 0).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, ROWS, 0xf, false));
+}
+
+// Maximum over the wave's 64 lanes: row shifts 1, 2, 4, 8 fold each row of 16
+// lanes into its lane 15, the row broadcasts 15 and 31 fold the rows into
+// lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<0x111, 0xf>(x));
+  x = max(x, dpp_u32<0x112, 0xf>(x));
+  x = max(x, dpp_u32<0x114, 0xf>(x));
+  x = max(x, dpp_u32<0x118, 0xf>(x));
+  x = max(x, dpp_u32<0x142, 0xa>(x));
+  x = max(x, dpp_u32<0x143, 0xc>(x));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+
+// The same m-th largest by repeated maxima: each round takes the largest
+// value left and sets the lanes holding it to 0 (the smallest key, so they
+// matter only when the answer is 0).  At most m rounds; cheaper than the 32
+// bisection steps for small m.
+__device__ __forceinline__ uint32_t wave_mth_largest(uint32_t x, uint32_t m) {
+  if (m > 8) return wave_mth_largest_bits(x, m);
+  for (;;) {
+    const uint32_t mx = wave_max_u32(x);
+    const uint32_t c = static_cast<uint32_t>(__popcll(__ballot(x == mx)));
+    if (c >= m || mx == 0) return mx;
+    m -= c;
+    x = x == mx ? 0u : x;
   }
+}
+
+// Inclusive prefix sum over the wave's 64 lanes, the same DPP pattern.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_u32<0x111, 0xf>(x);
+  x += dpp_u32<0x112, 0xf>(x);
+  x += dpp_u32<0x114, 0xf>(x);
+  x += dpp_u32<0x118, 0xf>(x);
+  x += dpp_u32<0x142, 0xa>(x);
+  x += dpp_u32<0x143, 0xc>(x);
   return x;
 }
 
