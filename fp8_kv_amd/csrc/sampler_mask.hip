@@ -488,15 +488,17 @@ __global__ __launch_bounds__(64) void cut_kernel(MaskParams p) {
                  : 0.f;
     lsum += w[e];
   }
-  // Wave prefix sum of the lane sums (fixed order: the result is
-  // deterministic), then each token's mass before it.
+  // Wave prefix sum of the lane sums (DPP row shifts and broadcasts: a fixed
+  // order, so the result is deterministic), then each token's mass before it.
+  auto fadd = [](float x, uint32_t y) { return x + __uint_as_float(y); };
   float incl = lsum;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const float y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
-  }
-  const float W = __shfl(incl, 63);
+  incl = fadd(incl, dpp_u32<0x111, 0xf>(__float_as_uint(incl)));
+  incl = fadd(incl, dpp_u32<0x112, 0xf>(__float_as_uint(incl)));
+  incl = fadd(incl, dpp_u32<0x114, 0xf>(__float_as_uint(incl)));
+  incl = fadd(incl, dpp_u32<0x118, 0xf>(__float_as_uint(incl)));
+  incl = fadd(incl, dpp_u32<0x142, 0xa>(__float_as_uint(incl)));
+  incl = fadd(incl, dpp_u32<0x143, 0xc>(__float_as_uint(incl)));
+  const float W = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
   float before = incl - lsum;
   int32_t keep = 0;
 #pragma unroll
@@ -506,8 +508,7 @@ __global__ __launch_bounds__(64) void cut_kernel(MaskParams p) {
     before += w[e];
   }
   // Kept tokens form a prefix of the order: the count is the largest keep.
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) keep = max(keep, __shfl_xor(keep, o));
+  keep = static_cast<int32_t>(wave_max_u32(static_cast<uint32_t>(keep)));
   // The kept tokens (a prefix of the order) for the masked write.
   for (int32_t i = lane; i < keep; i += 64) p.kept[static_cast<int64_t>(row) * p.k_max + i] = top[i];
   if (lane == 0) {
