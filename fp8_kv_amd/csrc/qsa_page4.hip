@@ -102,7 +102,9 @@ __device__ __forceinline__ Insert hash_insert(uint32_t* slots, uint32_t mask, in
 // distance M apart, every pair ascending: the lane with bit M clear keeps the
 // smaller value, its partner the larger.  Distances 1, 2, 4, 8 move the
 // partner's value with DPP (quad permutes, or row shifts within 16 lanes);
-// 16 and 32 with a lane shuffle.
+// 16 and 32 with gfx950's lane-swap instructions (v_permlane16_swap and
+// v_permlane32_swap with the value as both operands: the partner's value is
+// the first result in the lanes with bit M set, the second in the others).
 template <int M>
 __device__ __forceinline__ int32_t exchange(int32_t x) {
   const bool upper = (threadIdx.x & M) != 0;
@@ -114,7 +116,10 @@ __device__ __forceinline__ int32_t exchange(int32_t x) {
     const int32_t from_below = __builtin_amdgcn_update_dpp(0, x, 0x110 + M, 0xF, 0xF, false);
     return upper ? max(x, from_below) : min(x, from_above);
   } else {
-    const int32_t y = __shfl_xor(x, M);
+    static_assert(M == 16 || M == 32, "lane distances within a wave");
+    const auto r = M == 16 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                           : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    const int32_t y = static_cast<int32_t>(upper ? r[0] : r[1]);
     return upper ? max(x, y) : min(x, y);
   }
 }

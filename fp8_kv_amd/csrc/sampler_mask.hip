@@ -123,7 +123,9 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 
 // x from lane (lane ^ M): quad permutes for M = 1, 2, row shifts within 16
 // lanes for M = 4, 8 (lanes with bit M clear read lane + M, the others
-// lane - M), a lane shuffle for 16 and 32.
+// lane - M), gfx950's lane-swap instructions for 16 and 32 (the value as
+// both operands: the partner's value is the first result in the lanes with
+// bit M set, the second in the others).
 template <int M>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
   if constexpr (M == 1 || M == 2) {
@@ -133,7 +135,10 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
     const uint32_t down = __builtin_amdgcn_update_dpp(0u, x, 0x110 + M, 0xF, 0xF, false);
     return (threadIdx.x & M) ? down : up;
   } else {
-    return static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), M));
+    static_assert(M == 16 || M == 32, "lane distances within a wave");
+    const auto r = M == 16 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                           : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (threadIdx.x & M) ? r[0] : r[1];
   }
 }
 
