@@ -79,7 +79,7 @@ def cpu_baseline(case, budget_s: float) -> dict:
         oracle.paged_gqa(**case.oracle_kwargs())
         n_calls += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or n_calls >= 50:
+        if el >= budget_s or n_calls >= 200:
             break
     per_call = el / n_calls
     return {"value": round(case.kv_bytes_read() / per_call / 1e9, 4), "unit": "GB/s",
@@ -362,7 +362,7 @@ def main() -> int:
     ap.add_argument("--pools", type=int, default=8,
                     help="device copies of the KV pool rotated between steps (1 = warm cache)")
     ap.add_argument("--num-splits", type=int, default=0)
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying a captured graph")
