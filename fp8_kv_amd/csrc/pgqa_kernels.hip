@@ -17,7 +17,9 @@
 // online-softmax state; the four states are merged through LDS at the end.
 // In a whole call with unequal lengths the n*S workgroups of a kv head are
 // re-dealt by length (the balanced plan below), so short sequences leave no
-// workgroup idle.
+// workgroup idle.  With one split and many rows the decomposition is one
+// (row, kv head) per wave instead (RW): each wave walks all of its row's
+// tiles and stores its output itself, with no merge through LDS.
 // With one split the workgroup writes the fp16 output; with several it writes
 // a normalised fp32 partial and its base-2 log-sum-exp, merged by merge_kernel
 // in a second launch (a kernel boundary makes the partials visible; fencing
