@@ -12,7 +12,10 @@ Prints ONE JSON line.  `value` is KV-read GB/s: algorithmic KV bytes per call
 measured with HIP events on the stream the kernels run on.  `roofline` uses
 the dominant kernel alone (the attention kernel, timed the same way through
 paged_gqa_decode_partial with the same split plan); the whole call adds the
-split merge.
+split merge.  Beside them: `repeat` (the timed batch and four more of the same
+size), `warm` (one pool reused every call, so not an HBM rate) and, for
+decode, `read_ceiling` (a plain streaming read of the same number of bytes
+from the same rotated pools: the rate those bytes can reach here).
 """
 from __future__ import annotations
 
@@ -307,13 +310,16 @@ def bench_sampler(args) -> int:
     return 0
 
 
-def time_steps(step, steps: int, warmup: int, R: int, use_graph: bool) -> float:
+def time_batches(step, steps: int, warmup: int, R: int, use_graph: bool,
+                 batches: int = 1) -> list[float]:
     """Average milliseconds per step over exactly `steps` steps, timed with HIP
     events on the stream the kernels run on.  With use_graph the steps are
     captured into one HIP graph (up to kGraphSteps of them, cycling through the
     R pools, replayed as often as needed, the remainder eager), as a serving
     loop captures a whole decode step, so neither Python's per-call overhead
-    nor graph-launch boundaries leave the GPU idle between steps."""
+    nor graph-launch boundaries leave the GPU idle between steps.  Returns
+    one average per batch; every batch is exactly `steps` steps with its own
+    events."""
     import torch
 
     kGraphSteps = 512
@@ -342,15 +348,58 @@ def time_steps(step, steps: int, warmup: int, R: int, use_graph: bool) -> float:
     if use_graph and G > 0:
         replay()  # the graph's first launch uploads it: keep that out of the timing
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(cur)
-    for _ in range(steps // per_replay):
-        replay()
-    for i in range(steps % per_replay):
-        step(i)
-    e1.record(cur)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    out = []
+    for _ in range(batches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for _ in range(steps // per_replay):
+            replay()
+        for i in range(steps % per_replay):
+            step(i)
+        e1.record(cur)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    return out
+
+
+def time_steps(step, steps: int, warmup: int, R: int, use_graph: bool) -> float:
+    """Average milliseconds per step over exactly `steps` steps (one batch)."""
+    return time_batches(step, steps, warmup, R, use_graph)[0]
+
+
+def read_ceiling(pools, kv_bytes: int, steps: int, warmup: int, use_graph: bool) -> dict:
+    """The plain streaming-read kernel over the same number of KV bytes, taken
+    from the same rotated pools (K storage first, then V), timed like the
+    attention kernel; the best of a few grid sizes.  The attainable rate for
+    these bytes on this device, for context beside roofline.achieved."""
+    import torch
+
+    from fp8_kv_amd import stream_read as sr
+
+    R = len(pools)
+    spans = []
+    for p in pools:
+        ks, vs = (t.view(torch.uint8).reshape(-1) for t in p.storage)
+        if vs.data_ptr() == ks.data_ptr():      # interleaved: one allocation
+            spans.append((ks[:kv_bytes], None))
+        else:
+            half = kv_bytes // 2
+            spans.append((ks[:half], vs[:kv_bytes - half]))
+    sweep = {}
+    for blocks in (1024, 2048, 4096):
+        sink = torch.empty((blocks, 4), dtype=torch.int32, device="cuda")
+
+        def step(i, sink=sink, blocks=blocks):
+            a, b = spans[i % R]
+            sr.stream_read(a, b, sink, blocks)
+
+        sweep[blocks] = time_steps(step, steps, warmup, R, use_graph)
+    blocks = min(sweep, key=sweep.get)
+    ms = sweep[blocks]
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    return {"kernel": "stream_read_kernel (16-byte non-temporal loads, no page indirection)",
+            "us": round(ms * 1e3, 3), "GB/s": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "blocks": blocks, "sweep_us": {str(k): round(v * 1e3, 3) for k, v in sweep.items()}}
 
 
 def main() -> int:
@@ -421,7 +470,8 @@ def main() -> int:
                                       num_kv_heads=case.num_kv_heads,
                                       num_splits=args.num_splits)
 
-    ms = time_steps(call, args.steps, args.warmup, R, not args.eager)
+    batches = time_batches(call, args.steps, args.warmup, R, not args.eager, batches=5)
+    ms = batches[0]  # the timed K steps; the four batches after it show the spread
     # decode_partial runs the attention kernel of a whole call only when both
     # use the static split plan: decode (not prefill) with every length at
     # max_seq_len, or more sequences than the balanced plan covers.
@@ -471,6 +521,19 @@ def main() -> int:
                      "traffic": traffic if kernel_name == "attention_kernel" else None,
                      "kernel": kernel_name, "kernel_us": round(kernel_ms * 1e3, 3)},
     }
+    result["repeat"] = {"batches": len(batches), "steps_each": args.steps,
+                        "us_per_call": [round(b * 1e3, 3) for b in batches],
+                        "median_us": round(float(np.median(batches)) * 1e3, 3)}
+    if R > 1:
+        warm_ms = time_steps(lambda i: call(0), args.steps, args.warmup, 1, not args.eager)
+        result["warm"] = {
+            "pools_rotated": 1, "us_per_call": round(warm_ms * 1e3, 3),
+            "GB/s": round(kv_bytes / (warm_ms * 1e-3) / 1e9, 2),
+            "note": "one pool reused every call: its bytes can stay in the 256 MB last-level "
+                    "cache, so this is not an HBM rate"}
+    if not prefill:
+        result["read_ceiling"] = read_ceiling(pools, kv_bytes, args.steps, args.warmup,
+                                              not args.eager)
     if prefill:
         result["roofline"]["note"] = (
             "achieved counts gathered K/V bytes: rows select overlapping blocks of one pool, "

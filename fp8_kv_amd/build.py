@@ -1,4 +1,6 @@
-"""Build libpgqa.so (gfx950) in-tree with hipcc.
+"""Build libpgqa.so (gfx950) in-tree with hipcc, and beside it
+libstream_read.so, the plain streaming-read kernel the benchmark measures the
+attainable read rate with.
 
 Usage: python -m fp8_kv_amd.build   (or __graft_entry__.build()).
 """
@@ -14,6 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpgqa.so")
 SOURCES = ["pgqa_api.hip", "pgqa_kernels.hip", "qsa_api.hip", "qsa_page4.hip", "qsa_topk.hip",
            "sampler_api.hip", "sampler_mask.hip"]
+STREAM_LIB = os.path.join(PKG, "libstream_read.so")
+STREAM_SOURCES = ["stream_read.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -29,9 +33,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra: tuple[str, ...] = ()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+def _hipcc(lib: str, sources: list[str], verbose: bool, extra: tuple[str, ...]) -> str:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = lib + ".tmp"
     cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs,
            "-o", tmp]
     if verbose:
@@ -44,8 +48,14 @@ def build(verbose: bool = False, extra: tuple[str, ...] = ()) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False, extra: tuple[str, ...] = ()) -> str:
+    """Compiles both libraries; returns the path of libpgqa.so."""
+    _hipcc(STREAM_LIB, STREAM_SOURCES, verbose, extra)
+    return _hipcc(LIB, SOURCES, verbose, extra)
 
 
 if __name__ == "__main__":

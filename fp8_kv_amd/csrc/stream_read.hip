@@ -1,0 +1,120 @@
+// Plain streaming read of device memory: a measurement aid that sits beside
+// the attention path and is not part of it (its own library, libstream_read.so;
+// no attention entry point calls it).
+//
+// It reads the bytes of two buffers exactly once with 16-byte vector loads,
+// either non-temporal (the hint the decode kernels put on K and V loads, which
+// also keeps the bytes out of the last-level cache) or ordinary (as sparse
+// prefill reads its shared pool, so a warm buffer can be served from that
+// cache).  It computes nothing but an XOR checksum per workgroup, so the
+// loads cannot be dropped and a test can check that every byte was read.  Its rate is the read
+// bandwidth that those bytes can reach on this device with no page-table
+// indirection, no dependent round trips and no arithmetic: the ceiling the
+// attention kernel's KV rate is compared with (non-temporal, buffers rotated
+// for decode; ordinary loads over one warm pool for sparse prefill).
+//
+// Layout: the two buffers form one range of 16-byte words (all of a, then
+// all of b); workgroup w reads the contiguous words [w*C, (w+1)*C) of that
+// range, C = ceil(words / blocks) rounded up to 256 words (4 KiB), so each
+// wave instruction reads one aligned 1 KiB run.  sink[w] (16 bytes) receives
+// the XOR of the words workgroup w read (zero for a workgroup with none).
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;         // 16-byte loads in flight per thread
+constexpr int kMaxBlocks = 1 << 16;
+
+template <bool NT>
+__device__ inline u4_t load16(const u4_t* ptr) {
+  if constexpr (NT) return __builtin_nontemporal_load(ptr);
+  else return *ptr;
+}
+
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const u4_t* __restrict__ a,
+                                                               size_t na,
+                                                               const u4_t* __restrict__ b,
+                                                               size_t per_block, size_t n,
+                                                               u4_t* __restrict__ sink) {
+  const size_t begin = static_cast<size_t>(blockIdx.x) * per_block;
+  const size_t end = begin + per_block < n ? begin + per_block : n;
+  u4_t acc = {0u, 0u, 0u, 0u};
+  // i < end implies begin <= i < end <= n, so every index below stays in
+  // [begin, end): lanes past the end re-read word `begin` and drop it.
+  for (size_t i = begin + threadIdx.x; i < end; i += kThreads * kUnroll) {
+    u4_t v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const size_t j = i + static_cast<size_t>(u) * kThreads;
+      const size_t w = j < end ? j : begin;
+      const u4_t* ptr = w < na ? a + w : b + (w - na);
+      v[u] = load16<NT>(ptr);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const bool live = i + static_cast<size_t>(u) * kThreads < end;
+      acc ^= live ? v[u] : u4_t{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    acc.x ^= __shfl_xor(acc.x, off);
+    acc.y ^= __shfl_xor(acc.y, off);
+    acc.z ^= __shfl_xor(acc.z, off);
+    acc.w ^= __shfl_xor(acc.w, off);
+  }
+  __shared__ u4_t part[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    u4_t r = part[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) r ^= part[w];
+    sink[blockIdx.x] = r;
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+// Return codes: 0 success, -1 a required pointer is NULL, -2 a size is out
+// of range (blocks outside 1..65536, a byte count not a multiple of 16), -3
+// a pointer is not 16-byte aligned, -4 the launch failed.  Nothing is
+// launched on an error.
+//
+// a, b: device buffers of a_bytes and b_bytes (multiples of 16; a buffer of
+// 0 bytes may be NULL).  blocks: workgroups of 256 threads.  nontemporal:
+// nonzero for non-temporal loads, 0 for ordinary ones.  sink: device memory
+// of 16*blocks bytes, overwritten.  stream: a hipStream_t (NULL = the
+// default stream).  Asynchronous.
+int stream_read(const void* a, size_t a_bytes, const void* b, size_t b_bytes, int32_t blocks,
+                int32_t nontemporal, void* sink, void* stream) {
+  if (!sink || (a_bytes && !a) || (b_bytes && !b)) return -1;
+  if (blocks < 1 || blocks > kMaxBlocks || (a_bytes | b_bytes) % 16) return -2;
+  if (!aligned16(sink) || (a_bytes && !aligned16(a)) || (b_bytes && !aligned16(b))) return -3;
+  const size_t na = a_bytes / 16, n = na + b_bytes / 16;
+  size_t per_block = (n + blocks - 1) / blocks;
+  per_block = (per_block + kThreads - 1) / kThreads * kThreads;
+  const auto* pa = static_cast<const u4_t*>(a);
+  const auto* pb = static_cast<const u4_t*>(b);
+  auto* ps = static_cast<u4_t*>(sink);
+  const auto st = static_cast<hipStream_t>(stream);
+  if (nontemporal)
+    hipLaunchKernelGGL(stream_read_kernel<true>, dim3(blocks), dim3(kThreads), 0, st, pa, na, pb,
+                       per_block, n, ps);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<false>, dim3(blocks), dim3(kThreads), 0, st, pa, na,
+                       pb, per_block, n, ps);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // extern "C"

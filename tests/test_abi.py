@@ -283,3 +283,20 @@ def test_sampler_constants_match_header():
     import oracle
     assert (oracle.MASK_BAD_K, oracle.MASK_BAD_P) == (pgqa.SAMPLER_MASK_BAD_K,
                                                       pgqa.SAMPLER_MASK_BAD_P)
+
+
+def test_stream_read_library_validation():
+    """The streaming-read measurement library loads and rejects bad arguments
+    before launching anything."""
+    from fp8_kv_amd import stream_read as sr
+    lib = sr.load()
+    f = lib.stream_read
+    assert f(FAKE, 64, None, 0, 4, 1, None, None) == -1          # no sink
+    assert f(None, 64, None, 0, 4, 1, FAKE, None) == -1          # a missing
+    assert f(FAKE, 64, None, 16, 4, 1, FAKE, None) == -1         # b missing
+    assert f(FAKE, 64, None, 0, 0, 1, FAKE, None) == -2          # blocks
+    assert f(FAKE, 64, None, 0, sr.MAX_BLOCKS + 1, 1, FAKE, None) == -2
+    assert f(FAKE, 65, None, 0, 4, 1, FAKE, None) == -2          # not whole words
+    assert f(FAKE + 8, 64, None, 0, 4, 1, FAKE, None) == -3      # alignment
+    assert f(FAKE, 64, FAKE + 4, 16, 4, 1, FAKE, None) == -3
+    assert f(FAKE, 64, None, 0, 4, 1, FAKE + 8, None) == -3
