@@ -210,3 +210,48 @@ def test_prefill_through_built_table(dev, layout, tail):
     torch.cuda.synchronize()
     ref = oracle.paged_gqa(**view.oracle_kwargs())
     assert_parity(out.cpu().numpy(), ref, f"page4 prefill {layout} tail {tail}")
+
+
+def test_graph_replay_with_new_selections(dev):
+    """One captured build replayed after the selections and live lengths
+    change in place: each replay equals the oracle on the new inputs."""
+    from fp8_kv_amd import pgqa
+    cases = [inputs.page4_selection_case(rows=256, selected_blocks=120, tail=3, seq_blocks=2048,
+                                         page_size=16, order=o, seed=sd)
+             for o, sd in (("shuffled", 40), ("expanded", 41), ("blocks", 42))]
+    kw = cases[0].builder_kwargs()
+    tok = torch.from_numpy(cases[0].tokens).to(dev)
+    live = torch.from_numpy(cases[0].live_len).to(dev)
+    bt = torch.from_numpy(cases[0].block_table).to(dev)
+    rows = tok.shape[0]
+    t = torch.empty((rows, kw["out_stride"]), dtype=torch.int32, device=dev)
+    ln = torch.empty(rows, dtype=torch.int32, device=dev)
+    st = torch.empty(rows, dtype=torch.int32, device=dev)
+
+    def build(stream=None):
+        pgqa.qsa_build_page4_table(tok, live, bt, out_table=t, out_len=ln, out_status=st,
+                                   stream=stream, **kw)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        build(s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        build(s)
+    for c in cases[1:] + cases[:1]:
+        assert c.tokens.shape == cases[0].tokens.shape and c.builder_kwargs() == kw
+        print(f"page4 graph replay tokens {c.tokens.shape} live {c.live_len[:2]}", flush=True)
+        tok.copy_(torch.from_numpy(c.tokens))
+        live.copy_(torch.from_numpy(c.live_len))
+        bt.copy_(torch.from_numpy(c.block_table))
+        for x in (t, ln, st):
+            x.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle.qsa_page4_table(c.tokens, c.live_len, c.block_table, **kw)
+        for name, gv, rv in zip(("table", "len", "status"), (t, ln, st), ref):
+            assert np.array_equal(gv.cpu().numpy(), rv), name

@@ -504,3 +504,47 @@ def test_graph_replay_bitwise(pg):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager)
+
+
+def test_graph_replay_follows_new_lengths(pg):
+    """One captured decode call replayed after the device lengths change in
+    place: the split plan is made on the device from the lengths, so every
+    replay equals an eager call on the same lengths bit for bit, and the
+    oracle."""
+    import torch
+
+    case = inputs.decode_case(batch=4, lens=[4096] * 4, page_size=128, kv_dtype=E4M3,
+                              seed=77, scales="uniform", max_seq_len=4096)
+    q, pool, table, lens = pg.device_case(case)
+    n, hq, _ = q.shape
+    wsb = pg.paged_gqa_workspace_bytes(n, hq, 1, case.max_seq_len, 0)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+
+    def call(o, stream=None):
+        pg.paged_gqa_decode(q, pool, table, lens, case.max_seq_len, case.sm_scale, o,
+                            workspace=ws, stream=stream)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(out, s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(out, s)
+    for new in ([4096, 1, 0, 2000], [17, 4096, 4096, 3333], [0, 0, 0, 0], [4096] * 4,
+                [-3, 640, 64, 4095]):
+        print(f"graph replay lens={new}", flush=True)
+        lens.copy_(torch.tensor(new, dtype=torch.int32))
+        eager = torch.empty_like(q)
+        call(eager)
+        out.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), new
+        ref = oracle.paged_gqa(**dataclasses.replace(
+            case, lens=np.asarray(new, np.int32)).oracle_kwargs())
+        assert_parity(out.cpu().numpy(), ref, f"graph replay lens {new}")

@@ -152,3 +152,48 @@ def test_repeat_is_bitwise_identical(dev):
     a, _ = run_gpu(case.logits, case.k, case.p, dev)
     b, _ = run_gpu(case.logits, case.k, case.p, dev)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_graph_replay_with_new_logits(dev):
+    """One captured masking call replayed after the logits, k and p change in
+    place: each replay equals an eager call on the new inputs bit for bit."""
+    from fp8_kv_amd import pgqa
+    rows, V = 8, 248_320
+    cases = [inputs.sampler_case(rows=rows, vocab=V, k=k, p=p, seed=s)
+             for k, p, s in ((20, 0.95, 31), ([1, 256, 64, 20, 5, 100, 200, 2], 0.5, 32),
+                             (256, 1.0, 33))]
+    z = torch.from_numpy(cases[0].logits).to(dev)
+    kk = torch.from_numpy(np.array(cases[0].k, np.int32)).to(dev)
+    pp = torch.from_numpy(np.array(cases[0].p, np.float32)).to(dev)
+    out = torch.empty_like(z)
+    st = torch.empty(rows, dtype=torch.int32, device=dev)
+    ws = torch.empty(pgqa.sampler_topk_topp_workspace_bytes(rows, V), dtype=torch.uint8,
+                     device=dev)
+
+    def mask(o, so, stream=None):
+        pgqa.sampler_topk_topp_mask(z, kk, pp, out=o, status=so, workspace=ws, stream=stream)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        mask(out, st, s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        mask(out, st, s)
+    for c in cases[1:] + cases[:1]:
+        print(f"sampler graph replay k={np.unique(c.k)[:3]} p={np.unique(c.p)[:3]}", flush=True)
+        z.copy_(torch.from_numpy(c.logits))
+        kk.copy_(torch.from_numpy(np.array(c.k, np.int32)))
+        pp.copy_(torch.from_numpy(np.array(c.p, np.float32)))
+        eo = torch.empty_like(z)
+        es = torch.empty_like(st)
+        mask(eo, es)
+        out.fill_(3.0)
+        st.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), eo.view(torch.int32))
+        assert torch.equal(st, es)
