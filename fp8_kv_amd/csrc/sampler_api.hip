@@ -36,6 +36,11 @@ int sampler_topk_topp_mask(const float* logits, int64_t row_stride, int32_t rows
   if (rows == 0) return PGQA_OK;
   if (!logits || !k || !p || !out) return PGQA_ERR_NULL;
   if (row_stride < vocab || out_stride < vocab) return PGQA_ERR_LAYOUT;
+  // In place needs equal strides; otherwise the two row ranges may not meet.
+  const uintptr_t z0 = reinterpret_cast<uintptr_t>(logits), o0 = reinterpret_cast<uintptr_t>(out);
+  const uintptr_t z1 = z0 + ((rows - 1) * static_cast<uint64_t>(row_stride) + vocab) * 4;
+  const uintptr_t o1 = o0 + ((rows - 1) * static_cast<uint64_t>(out_stride) + vocab) * 4;
+  if (z0 == o0 ? out_stride != row_stride : (z0 < o1 && o0 < z1)) return PGQA_ERR_LAYOUT;
   if (!aligned(logits, 4) || !aligned(k, 4) || !aligned(p, 4) || !aligned(out, 4) ||
       !aligned(status, 4))
     return PGQA_ERR_LAYOUT;

@@ -490,10 +490,15 @@ def page4_view(kv: PagedCase, table: np.ndarray, lens: np.ndarray) -> PagedCase:
     given per-row tables and lengths."""
     ts = kv.token_stride
     assert kv.page_stride % (4 * ts) == 0
-    vpp = kv.page_stride // (4 * ts)
+    # As many view pages as keep both K and V of the last one inside their
+    # storage (interleaved pools: the views over a page's V half have no V
+    # rows of their own, so the final few ids are left out).
+    last = 3 * ts + (kv.num_kv_heads - 1) * kv.head_stride + kv.head_dim  # one page's reach
+    room = min(kv.k_store.size - kv.k_offset, kv.v_store.size - kv.v_offset)
+    num_pages = (room - last) // (4 * ts) + 1
     return PagedCase(q=kv.q, k_store=kv.k_store, v_store=kv.v_store, k_offset=kv.k_offset,
                      v_offset=kv.v_offset, page_stride=4 * ts, token_stride=ts,
-                     head_stride=kv.head_stride, num_pages=kv.num_pages * vpp, page_size=4,
+                     head_stride=kv.head_stride, num_pages=num_pages, page_size=4,
                      kv_dtype=kv.kv_dtype, k_scale=kv.k_scale, v_scale=kv.v_scale,
                      table=np.ascontiguousarray(table, dtype=np.int32),
                      lens=np.ascontiguousarray(lens, dtype=np.int32),

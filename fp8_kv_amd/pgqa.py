@@ -2,8 +2,11 @@
 
 Every function has the name of the C entry point it calls.  Tensors are
 torch tensors on the GPU (PyTorch provides device memory and streams); the
-computation is done entirely by the library's HIP kernels.  There is no
-fallback: if ``libpgqa.so`` is missing the first call raises.
+computation is done entirely by the library's HIP kernels.  The library sees
+only pointers, so before each call the binding checks what the tensors say
+about them (dtype, shape, layout, device, and that a KV pool's tensors hold
+every element its strides address) and raises ValueError otherwise.  There
+is no fallback: if ``libpgqa.so`` is missing the first call raises.
 """
 from __future__ import annotations
 
@@ -153,6 +156,54 @@ def _check(rc: int, where: str) -> None:
         raise PgqaError(rc, where)
 
 
+def _expect(t, name: str, dtype, shape=None, *, dense: bool = True) -> None:
+    """Checks a tensor before its address goes to the library, which sees only
+    pointers: dtype, shape (None matches any size) and dense row-major layout
+    when the C side assumes one.  _device checks where it lives, after every
+    tensor of a call has passed these."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and (t.dim() != len(shape) or
+                              any(w is not None and w != d for w, d in zip(shape, t.shape))):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dense and not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _device(**tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name}: must be a device tensor")
+
+
+def _bytes_after(t) -> int:
+    """Bytes of t's storage from t.data_ptr() to the storage's end."""
+    st = t.untyped_storage()
+    return st.nbytes() - (t.data_ptr() - st.data_ptr())
+
+
+def _pool_extent(kv: "KVPool", num_kv_heads: int) -> int | None:
+    """Bytes from K's (and V's) start to the end of the farthest element the
+    strides address, (num_pages-1, page_size-1, num_kv_heads-1, 255); None
+    for sizes the library rejects by itself."""
+    dims = (kv.num_pages, kv.page_size, num_kv_heads)
+    strides = (kv.page_stride, kv.token_stride, kv.head_stride)
+    if min(dims) < 1 or min(strides) < 0:
+        return None
+    es = 1 if kv.kv_dtype == PGQA_KV_E4M3 else 2
+    return (sum((d - 1) * st for d, st in zip(dims, strides)) + HEAD_DIM) * es
+
+
+def _check_pool(kv: "KVPool", num_kv_heads: int) -> None:
+    extent = _pool_extent(kv, num_kv_heads)
+    if extent is None:
+        return
+    for name, t in (("kv.k", kv.k), ("kv.v", kv.v)):
+        if _bytes_after(t) < extent:
+            raise ValueError(f"{name}: {_bytes_after(t)} bytes from its start, the strides "
+                             f"address {extent}")
+
+
 def paged_gqa_workspace_bytes(n: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int,
                               num_splits: int = 0, head_dim: int = HEAD_DIM) -> int:
     r = _lib().paged_gqa_workspace_bytes(n, num_q_heads, num_kv_heads, head_dim, max_seq_len,
@@ -187,8 +238,26 @@ def paged_gqa_prefill_sparse(q, kv: KVPool, row_tables, row_lens, max_row_len: i
           sm_scale, num_splits, out, workspace, stream)
 
 
+def _check_inputs(q, kv, table, lens, hkv) -> None:
+    import torch
+
+    _expect(q, "q", torch.float16, (None, None, None))
+    n = q.shape[0]
+    _expect(table, "page table", torch.int32, (n, None))
+    _expect(lens, "lengths", torch.int32, (n,))
+    _check_pool(kv, hkv)
+
+
 def _call(fn_name, q, kv, table, lens, max_len, hkv, sm_scale, num_splits, out, workspace,
           stream):
+    import torch
+
+    _check_inputs(q, kv, table, lens, hkv)
+    _expect(out, "out", torch.float16, tuple(q.shape))
+    if workspace is not None:
+        _expect(workspace, "workspace", workspace.dtype)
+    _device(q=q, page_table=table, lengths=lens, kv_k=kv.k, kv_v=kv.v, out=out,
+            workspace=workspace)
     n, hq, d = q.shape
     c_pool = kv.as_c()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -204,7 +273,15 @@ def paged_gqa_decode_partial(q, kv: KVPool, page_table, seq_lens, max_seq_len: i
                              num_splits: int = 0, stream=None) -> None:
     """part_o: fp32 [B][Hq][S][256]; part_lse: fp32 [B][Hq][S] with
     S = paged_gqa_num_splits(B, num_kv_heads, max_seq_len, num_splits)."""
+    import torch
+
+    _check_inputs(q, kv, page_table, seq_lens, num_kv_heads)
     n, hq, d = q.shape
+    S = paged_gqa_num_splits(n, num_kv_heads, max_seq_len, num_splits)
+    _expect(part_o, "part_o", torch.float32, (n, hq, S, d))
+    _expect(part_lse, "part_lse", torch.float32, (n, hq, S))
+    _device(q=q, page_table=page_table, lengths=seq_lens, kv_k=kv.k, kv_v=kv.v, part_o=part_o,
+            part_lse=part_lse)
     c_pool = kv.as_c()
     rc = _lib().paged_gqa_decode_partial(
         _ptr(q), ctypes.byref(c_pool), _ptr(page_table), int(page_table.shape[1]),
@@ -216,8 +293,18 @@ def paged_gqa_decode_partial(q, kv: KVPool, page_table, seq_lens, max_seq_len: i
 def paged_gqa_merge_partials(part_o, part_lse, out, stream=None) -> None:
     """part_o: fp32 [rows][S][256]; part_lse: fp32 [rows][S]; out: fp16 [rows][256]
     (any leading shape that flattens to these)."""
-    splits = part_lse.shape[-1]
-    rows = part_lse.numel() // splits
+    import torch
+
+    _expect(part_lse, "part_lse", torch.float32)
+    splits = part_lse.shape[-1] if part_lse.dim() else 0
+    rows = part_lse.numel() // splits if splits else 0
+    _expect(part_o, "part_o", torch.float32)
+    _expect(out, "out", torch.float16)
+    d = part_o.shape[-1] if part_o.dim() else 0
+    if part_o.numel() != rows * splits * d or out.numel() != rows * d:
+        raise ValueError(f"part_o {tuple(part_o.shape)} / out {tuple(out.shape)} do not hold "
+                         f"{rows} rows of {splits} splits")
+    _device(part_o=part_o, part_lse=part_lse, out=out)
     rc = _lib().paged_gqa_merge_partials(_ptr(part_o), _ptr(part_lse), int(rows), int(splits),
                                          int(part_o.shape[-1]), _ptr(out),
                                          _stream_handle(stream))
@@ -226,6 +313,10 @@ def paged_gqa_merge_partials(part_o, part_lse, out, stream=None) -> None:
 
 def e4m3_decode_table(out, stream=None) -> None:
     """out: float32 [256] device tensor."""
+    import torch
+
+    _expect(out, "out", torch.float32, (256,))
+    _device(out=out)
     _check(_lib().e4m3_decode_table(_ptr(out), _stream_handle(stream)), "e4m3_decode_table")
 
 
@@ -243,10 +334,19 @@ def qsa_topk_select(scores, k: int, n_valid=None, n_blocks: int | None = None, o
         raise ValueError("scores must be a float32 [rows][n] tensor with unit column stride")
     rows = scores.shape[0]
     nb = scores.shape[1] if n_blocks is None else int(n_blocks)
+    if nb > scores.shape[1] and rows > 0:
+        raise ValueError(f"n_blocks {nb} exceeds the {scores.shape[1]} score columns")
+    if n_valid is not None:
+        _expect(n_valid, "n_valid", torch.int32, (rows,))
     if out_idx is None:
         out_idx = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    elif k > 0:
+        _expect(out_idx, "out_idx", torch.int32, (rows, k))
     if out_count is None:
         out_count = torch.empty(rows, dtype=torch.int32, device=scores.device)
+    else:
+        _expect(out_count, "out_count", torch.int32, (rows,))
+    _device(scores=scores, n_valid=n_valid, out_idx=out_idx, out_count=out_count)
     stride = scores.stride(0) if rows > 1 else max(scores.shape[1], nb)
     rc = _lib().qsa_topk_select(_ptr(scores), int(stride), _ptr(n_valid), int(rows), int(nb),
                                 int(k), _ptr(out_idx) if k > 0 else None, _ptr(out_count),
@@ -273,12 +373,23 @@ def qsa_build_page4_table(tokens, live_len, block_table, *, num_pages: int, page
         raise ValueError("block_table must be a contiguous int32 [n_seqs][max_pages] tensor")
     rows, n = tokens.shape
     dev = tokens.device
+    _expect(live_len, "live_len", torch.int32, (rows,))
+    if row_seq is not None:
+        _expect(row_seq, "row_seq", torch.int32, (rows,))
     if out_table is None:
         out_table = torch.empty((rows, out_stride), dtype=torch.int32, device=dev)
+    else:
+        _expect(out_table, "out_table", torch.int32, (rows, out_stride))
     if out_len is None:
         out_len = torch.empty(rows, dtype=torch.int32, device=dev)
+    else:
+        _expect(out_len, "out_len", torch.int32, (rows,))
     if out_status is None:
         out_status = torch.empty(rows, dtype=torch.int32, device=dev)
+    else:
+        _expect(out_status, "out_status", torch.int32, (rows,))
+    _device(tokens=tokens, live_len=live_len, block_table=block_table, row_seq=row_seq,
+            out_table=out_table, out_len=out_len, out_status=out_status)
     stride = tokens.stride(0) if rows > 1 and n > 0 else n
     rc = _lib().qsa_build_page4_table(
         _ptr(tokens), int(stride), int(n), _ptr(live_len), _ptr(block_table),
@@ -308,13 +419,24 @@ def sampler_topk_topp_mask(logits, k, p, *, k_max: int = SAMPLER_MAX_K, out=None
         raise ValueError("logits must be a float32 [rows][vocab] tensor with unit column stride")
     rows, vocab = logits.shape
     dev = logits.device
+    _expect(k, "k", torch.int32, (rows,))
+    _expect(p, "p", torch.float32, (rows,))
     if out is None:
         out = torch.empty_like(logits)
+    else:
+        _expect(out, "out", torch.float32, (rows, vocab), dense=False)
+        if vocab > 1 and out.stride(1) != 1:
+            raise ValueError("out must have unit column stride")
     if status is None:
         status = torch.empty(rows, dtype=torch.int32, device=dev)
+    else:
+        _expect(status, "status", torch.int32, (rows,))
     if workspace is None:
         wsb = sampler_topk_topp_workspace_bytes(rows, vocab, k_max)
         workspace = torch.empty(max(wsb, 8), dtype=torch.uint8, device=dev)
+    else:
+        _expect(workspace, "workspace", workspace.dtype)
+    _device(logits=logits, k=k, p=p, out=out, status=status, workspace=workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     stride = logits.stride(0) if rows > 1 else vocab
     ostride = out.stride(0) if rows > 1 else vocab

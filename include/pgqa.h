@@ -342,7 +342,8 @@ int qsa_build_page4_table(const int32_t* tokens, int64_t token_stride, int32_t n
  *                bytes; caller-owned, contents need no initialisation.
  * Runs three kernels on `stream`; nothing is allocated.
  * Errors: PGQA_ERR_SHAPE (rows, vocab or k_max out of range), PGQA_ERR_NULL,
- * PGQA_ERR_LAYOUT (a stride below vocab or a misaligned pointer),
+ * PGQA_ERR_LAYOUT (a stride below vocab, a misaligned pointer, out equal
+ * to logits with another stride, or out overlapping logits otherwise),
  * PGQA_ERR_WORKSPACE, PGQA_ERR_HIP.
  */
 #define SAMPLER_MAX_K 256

@@ -263,6 +263,9 @@ def test_sampler_validation(lib):
         assert call(**{name: None}) == pgqa.PGQA_ERR_NULL, name
     assert call(stride=999) == pgqa.PGQA_ERR_LAYOUT
     assert call(ostride=999) == pgqa.PGQA_ERR_LAYOUT
+    assert call(ostride=1004) == pgqa.PGQA_ERR_LAYOUT       # in place, other stride
+    assert call(out=FAKE + 4 * 16) == pgqa.PGQA_ERR_LAYOUT  # partial overlap
+    assert call(out=FAKE - 4 * 3996) == pgqa.PGQA_ERR_LAYOUT  # ends inside logits
     for name in ("z", "k", "p", "out", "st"):
         assert call(**{name: FAKE + 2}) == pgqa.PGQA_ERR_LAYOUT, name
     assert call(ws=None) == pgqa.PGQA_ERR_WORKSPACE
