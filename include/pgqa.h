@@ -251,7 +251,10 @@ int qsa_topk_select(const float* scores, int64_t row_stride, const int32_t* n_va
  * are clamped away and invalid requests are inert).  The result is what
  * paged_gqa_prefill_sparse takes as row_tables / row_lens with page_size 4
  * over the view: k_base and v_base unchanged, page_stride = 4 * token_stride,
- * num_pages = num_pages * vpages_per_page.
+ * num_pages = the view pages whose K and V rows both lie in the pool:
+ * num_pages * vpages_per_page for separate K and V arrays; an interleaved
+ * pool (each page's V rows after its K rows) loses the last few views of its
+ * final page, which lie over V rows and are never emitted here.
  *
  * Per row r, with L = live_len[r] and c = (L - 1) / 4 (the 4-token block that
  * holds the row's own position):
