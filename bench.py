@@ -261,7 +261,7 @@ def cpu_baseline_sampler(case, budget_s: float) -> dict:
 
 def bench_sampler(args) -> int:
     """Combined top-k/top-p masking: one step = one sampler_topk_topp_mask
-    call over every row (three kernels).  `value` is the call's algorithmic
+    call over every row (two kernels).  `value` is the call's algorithmic
     bytes (every logit read once and written once) per average call time."""
     import torch
 
@@ -301,7 +301,7 @@ def bench_sampler(args) -> int:
                    "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "chunk_top_kernel + cut_kernel + apply_kernel",
+                     "kernel": "chunk_top_kernel + cut_kernel",
                      "kernel_us": round(ms * 1e3, 3)},
     }
     if not args.no_cpu_baseline:

@@ -59,8 +59,6 @@ int sampler_topk_topp_mask(const float* logits, int64_t row_stride, int32_t rows
   m.status = status;
   sampler::plan_chunks(vocab, &m.chunk, &m.n_chunks);
   m.cand = static_cast<uint64_t*>(workspace);
-  m.cut = m.cand + static_cast<size_t>(rows) * m.n_chunks * k_max;
-  m.kept = m.cut + rows;
   if (sampler::launch_mask(m, static_cast<hipStream_t>(stream)) != hipSuccess)
     return PGQA_ERR_HIP;
   return PGQA_OK;

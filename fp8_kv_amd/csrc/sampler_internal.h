@@ -32,8 +32,6 @@ struct MaskParams {
   int32_t chunk;           // logits per chunk (multiple of 1024)
   int32_t n_chunks;        // <= kMaxChunks
   uint64_t* cand;          // workspace [rows][k_max][n_chunks] chunk top lists, rank-major
-  uint64_t* cut;           // workspace [rows]: number of kept tokens, 0 = copy the row
-  uint64_t* kept;          // workspace [rows][k_max]: the kept tokens in order
 };
 
 // Chunk size and count for a vocabulary; chunk = 0 when it is too large.

@@ -11,25 +11,26 @@
 //   n); kept tokens keep their logit, every other token becomes -inf.
 //
 // A token is represented by the 64-bit value (key << 32) | ~index: larger
-// means earlier in the order, and all such values are distinct.  The kept
-// tokens are exactly those at or above the last kept token's value (the
-// row's "cut"), so the masked row is one comparison per logit.
+// means earlier in the order, and all such values are distinct, and the key
+// gives back the logit's fp32 bits exactly.  The kept tokens are a prefix
+// of the order, at most k <= 256 of them.
 //
-// Three launches:
+// Two launches:
 //   1. chunk_top_kernel, one 256-thread workgroup per (chunk of <= 8192
 //      logits, row): the chunk's top min(k, chunk) tokens in order.  A
 //      threshold T from the lane maxima (each of the four waves contributes
 //      ceil(k/4) lanes whose maximum is >= T, so at least k keys are >= T)
 //      leaves a few candidates; one wave sorts up to 512 of them in
-//      registers, more (ties, large k) go through an LDS bitonic sort.
+//      registers, more (ties, large k) go through an LDS bitonic sort.  The
+//      same workgroup writes -inf over its chunk of the output once its
+//      logits are in registers (or copies the chunk for an invalid row), so
+//      the logits are read once and every output element written once.
 //   2. cut_kernel, one wave per row: the top-k set in order from the <= 64
 //      sorted chunk lists (the list prefixes at or above the k-th largest
 //      list head, sorted in registers; a tournament over the list heads when
 //      there are too many); then the softmax masses in fp32 (exp2 with
-//      log2(e) folded in), a wave prefix sum, and the cut.
-//   3. apply_kernel: -inf over the row, then the kept tokens' logits
-//      scattered back (a token's key gives back its fp32 bits exactly), so
-//      the logits are not read again; rows that are invalid are copied.
+//      log2(e) folded in), a wave prefix sum, the kept count, and the kept
+//      tokens' logits written back over the -inf.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -241,15 +242,38 @@ __global__ __launch_bounds__(kThreads) void chunk_top_kernel(MaskParams p) {
     const int32_t e = tid + kThreads * i;
     key[i] = e < len ? __float_as_uint(src[e]) : 0xFFFFFFFFu;
   }
+  float* out = p.out + static_cast<int64_t>(row) * p.out_stride + start;
+  const bool in_place = p.out == p.logits;  // then the strides are equal
   int32_t k;
   float pp;
-  if (!row_valid(p, row, k, pp)) return;  // the row is copied by apply_kernel
+  if (!row_valid(p, row, k, pp)) {
+    // An invalid row is copied unchanged (in place it already is).
+    if (!in_place) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int32_t e = tid + kThreads * i;
+        if (e < len) out[e] = __uint_as_float(key[i]);
+      }
+    }
+    return;
+  }
   const int32_t kc = min(k, len);
   uint32_t lmax = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     key[i] = key_of(__uint_as_float(key[i]));  // 0xFFFFFFFF (past the chunk) -> key 0
     lmax = max(lmax, key[i]);
+  }
+  // -inf over the chunk: each thread overwrites only the entries it has
+  // already read into registers, so this is safe in place too.  The kept
+  // logits are written back by cut_kernel, after this launch has finished.
+  // (Issuing it before the loads return, into a separate output, measured
+  // no faster.)
+  const float ninf = -__builtin_huge_valf();
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int32_t e = tid + kThreads * i;
+    if (e < len) out[e] = ninf;
   }
 
   // Threshold: each wave's ceil(kc/4)-th largest lane maximum; T = their
@@ -390,12 +414,9 @@ __global__ __launch_bounds__(64) void cut_kernel(MaskParams p) {
   }
   int32_t k;
   float pp;
-  if (!row_valid(p, row, k, pp)) {
-    if (lane == 0) {
-      p.cut[row] = 0;
-      if (p.status) p.status[row] = (k >= 1 && k <= p.k_max ? 0 : kBadK) |
-                                    (__builtin_isnan(pp) ? kBadP : 0);
-    }
+  if (!row_valid(p, row, k, pp)) {  // copied by chunk_top_kernel
+    if (lane == 0 && p.status)
+      p.status[row] = (k >= 1 && k <= p.k_max ? 0 : kBadK) | (__builtin_isnan(pp) ? kBadP : 0);
     return;
   }
   const int32_t n = min(k, p.vocab);
@@ -514,67 +535,18 @@ __global__ __launch_bounds__(64) void cut_kernel(MaskParams p) {
   }
   // Kept tokens form a prefix of the order: the count is the largest keep.
   keep = static_cast<int32_t>(wave_max_u32(static_cast<uint32_t>(keep)));
-  // The kept tokens (a prefix of the order) for the masked write.
-  for (int32_t i = lane; i < keep; i += 64) p.kept[static_cast<int64_t>(row) * p.k_max + i] = top[i];
-  if (lane == 0) {
-    p.cut[row] = static_cast<uint64_t>(keep);
-    if (p.status) p.status[row] = 0;
+  // The kept tokens (a prefix of the order) get their logits back; the
+  // rest of the row holds the -inf chunk_top_kernel wrote.
+  // Every kept entry is a real token (list padding is the value 0, below all
+  // of them, and there are at least n real ones); the range check keeps the
+  // store inside the row regardless.
+  float* out = p.out + static_cast<int64_t>(row) * p.out_stride;
+  for (int32_t i = lane; i < keep; i += 64) {
+    const uint64_t t = top[i];
+    const uint32_t idx = ~static_cast<uint32_t>(t);
+    if (idx < static_cast<uint32_t>(p.vocab)) out[idx] = value_of(static_cast<uint32_t>(t >> 32));
   }
-}
-
-// One workgroup per (row, 4096 logits).  A valid row: -inf over the range,
-// then each kept token inside it written back (at most k_max <= 256 kept
-// tokens, one per thread); the barrier orders the two stores of a kept
-// position.  An invalid row (count 0) is copied.  Unless the call is in
-// place, the fill is issued before the count arrives; an invalid row's copy
-// then rewrites exactly the positions each thread filled, so program order
-// puts the copy last.  VEC: rows 16-byte aligned (strides multiples of 4).
-template <bool VEC>
-__global__ __launch_bounds__(256) void apply_kernel(MaskParams p) {
-  const int row = blockIdx.y;
-  const int32_t base = blockIdx.x * (256 * 16);
-  const int32_t end = min(base + 256 * 16, p.vocab);
-  const float* src = p.logits + static_cast<int64_t>(row) * p.row_stride;
-  float* dst = p.out + static_cast<int64_t>(row) * p.out_stride;
-  const bool in_place = src == dst;
-  const uint64_t nk = p.cut[row];
-  uint64_t tok = 0;
-  if (threadIdx.x < nk) tok = p.kept[static_cast<int64_t>(row) * p.k_max + threadIdx.x];
-  const float ninf = -__builtin_huge_valf();
-  // fill(true) writes -inf, fill(false) copies the row; both touch the same
-  // positions from the same thread.
-  auto fill = [&](bool minus_inf) {
-    if constexpr (VEC) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t t = base + 4 * (256 * i + static_cast<int32_t>(threadIdx.x));
-        if (t + 4 <= end) {
-          *reinterpret_cast<float4*>(dst + t) =
-              minus_inf ? make_float4(ninf, ninf, ninf, ninf)
-                        : *reinterpret_cast<const float4*>(src + t);
-        } else {
-          for (int32_t u = t; u < end; ++u) dst[u] = minus_inf ? ninf : src[u];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int32_t t = base + 256 * i + static_cast<int32_t>(threadIdx.x);
-        if (t < end) dst[t] = minus_inf ? ninf : src[t];
-      }
-    }
-  };
-  if (!in_place) fill(true);
-  if (nk == 0) {
-    if (!in_place) fill(false);  // in place, the row already is its own copy
-    return;
-  }
-  if (in_place) fill(true);
-  __syncthreads();
-  if (threadIdx.x < nk) {
-    const int32_t t = static_cast<int32_t>(~static_cast<uint32_t>(tok));
-    if (t >= base && t < end) dst[t] = value_of(static_cast<uint32_t>(tok >> 32));
-  }
+  if (lane == 0 && p.status) p.status[row] = 0;
 }
 
 }  // namespace
@@ -595,8 +567,7 @@ void plan_chunks(int32_t vocab, int32_t* chunk, int32_t* n_chunks) {
 size_t workspace_bytes(int32_t rows, int32_t vocab, int32_t k_max) {
   int32_t chunk = 0, n_chunks = 0;
   plan_chunks(vocab, &chunk, &n_chunks);
-  const size_t cand = sizeof(uint64_t) * static_cast<size_t>(rows) * n_chunks * k_max;
-  return cand + sizeof(uint64_t) * static_cast<size_t>(rows) * (1 + k_max);
+  return sizeof(uint64_t) * static_cast<size_t>(rows) * n_chunks * k_max;
 }
 
 hipError_t launch_mask(const MaskParams& p, hipStream_t stream) {
@@ -628,14 +599,6 @@ hipError_t launch_mask(const MaskParams& p, hipStream_t stream) {
     if (raised != hipSuccess) return raised;
   }
   hipLaunchKernelGGL(cut_kernel, dim3(p.rows), dim3(64), lds, stream, p);
-  const unsigned blocks = static_cast<unsigned>((p.vocab + 256 * 16 - 1) / (256 * 16));
-  const bool vec = (reinterpret_cast<uintptr_t>(p.logits) & 15u) == 0 &&
-                   (reinterpret_cast<uintptr_t>(p.out) & 15u) == 0 && p.row_stride % 4 == 0 &&
-                   p.out_stride % 4 == 0;
-  if (vec)
-    hipLaunchKernelGGL(apply_kernel<true>, dim3(blocks, p.rows), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(apply_kernel<false>, dim3(blocks, p.rows), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

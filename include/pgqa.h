@@ -343,7 +343,7 @@ int qsa_build_page4_table(const int32_t* tokens, int64_t token_stride, int32_t n
  *   workspace    device memory, 8-byte aligned, at least
  *                sampler_topk_topp_workspace_bytes(rows, vocab, k_max)
  *                bytes; caller-owned, contents need no initialisation.
- * Runs three kernels on `stream`; nothing is allocated.
+ * Runs two kernels on `stream`; nothing is allocated.
  * Errors: PGQA_ERR_SHAPE (rows, vocab or k_max out of range), PGQA_ERR_NULL,
  * PGQA_ERR_LAYOUT (a stride below vocab, a misaligned pointer, out equal
  * to logits with another stride, or out overlapping logits otherwise),
