@@ -184,14 +184,19 @@ def decode_case(*, batch: int, lens, page_size: int, kv_dtype: int,
 def sparse_prefill_case(*, rows: int, selected_blocks: int, tail: int, pool_blocks: int,
                         layout: str = "interleaved", seed: int = 0, num_q_heads: int = 6,
                         num_kv_heads: int = 1, head_dim: int = 256,
-                        kv_dtype: int = KV_FP16, scales="unit", page_size: int = 4) -> PagedCase:
+                        kv_dtype: int = KV_FP16, scales="unit", page_size: int = 4,
+                        share_rows: int = 1) -> PagedCase:
     """Sparse prefill through virtual page tables (page-4 by default).
 
     Row r owns block c_r = pool_blocks - rows + r (its causal block).  It
     selects `selected_blocks` distinct blocks uniformly from [0, c_r), sorted
     increasingly (locality order), then the partial page: the first `tail`
     tokens of block c_r (tail = 0 means no partial page).  Row length is
-    page_size*selected_blocks + tail.
+    page_size*selected_blocks + tail.  With share_rows = G > 1, each group of
+    G consecutive rows shares one selection, drawn below the causal block of
+    the group's first row (a stand-in for the overlap of neighbouring query
+    rows' selections; the pages do not describe it).  share_rows = 1 draws
+    exactly as before.
     """
     P = page_size
     assert 0 <= tail < P and pool_blocks - rows >= selected_blocks
@@ -201,8 +206,9 @@ def sparse_prefill_case(*, rows: int, selected_blocks: int, tail: int, pool_bloc
     tab = np.empty((rows, n_entries), dtype=np.int32)
     for r in range(rows):
         c_r = pool_blocks - rows + r
-        sel = rt.choice(c_r, size=selected_blocks, replace=False, shuffle=False)
-        tab[r, :selected_blocks] = np.sort(sel)
+        if r % share_rows == 0:
+            sel = np.sort(rt.choice(c_r, size=selected_blocks, replace=False, shuffle=False))
+        tab[r, :selected_blocks] = sel
         if tail:
             tab[r, selected_blocks] = c_r
     L = P * selected_blocks + tail
@@ -219,7 +225,8 @@ def sparse_prefill_case(*, rows: int, selected_blocks: int, tail: int, pool_bloc
                      k_scale=k_scale, v_scale=v_scale, table=tab,
                      lens=np.full(rows, L, dtype=np.int32), max_seq_len=L,
                      sm_scale=1.0 / np.sqrt(head_dim), num_kv_heads=num_kv_heads,
-                     layout=layout, meta=dict(selected_blocks=selected_blocks, tail=tail))
+                     layout=layout, meta=dict(selected_blocks=selected_blocks, tail=tail,
+                                              share_rows=share_rows))
 
 
 # The five workloads, by what they are.
@@ -237,6 +244,11 @@ WORKLOADS = {
     "prefill_sparse_4096x2051_p4": dict(kind="prefill", rows=4096, selected_blocks=512,
                                          tail=3, pool_blocks=65536, layout="interleaved",
                                          seed=0),
+    # The same shape with groups of 32 consecutive rows sharing a selection.
+    "prefill_sparse_4096x2051_p4_shared32": dict(kind="prefill", rows=4096,
+                                                  selected_blocks=512, tail=3,
+                                                  pool_blocks=65536, layout="interleaved",
+                                                  seed=0, share_rows=32),
     # The page-16 selected-context sweep at 4096 rows (64, 512, 2048 tokens).
     "prefill_sparse_4096x64_p16": dict(kind="prefill", rows=4096, selected_blocks=4, tail=0,
                                         pool_blocks=16384, page_size=16,
