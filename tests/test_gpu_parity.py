@@ -548,3 +548,44 @@ def test_graph_replay_follows_new_lengths(pg):
         ref = oracle.paged_gqa(**dataclasses.replace(
             case, lens=np.asarray(new, np.int32)).oracle_kwargs())
         assert_parity(out.cpu().numpy(), ref, f"graph replay lens {new}")
+
+
+# ------------------------------------------------------ seeded random sweep
+def _sweep_case(i: int):
+    """Configuration i of the sweep: batch, lengths (with empty and negative
+    ones), page size, kv heads, group size, dtype, layout, scales and split
+    count all drawn from one seeded generator.  The V scale stays <= 1.5 so
+    that |o| < 8, where half an fp16 unit in the last place is below the
+    2e-3 bar."""
+    rng = np.random.default_rng(5000 + i)
+    hkv = int(rng.choice([1, 1, 2, 3]))
+    group = int(rng.choice([1, 2, 4, 6, 6, 8, 16]))
+    P = int(rng.choice([1, 3, 4, 7, 16, 32, 100, 128, 256, 300]))
+    batch = int(rng.integers(1, 41))
+    lmax = int(rng.choice([1, 40, 700, 3000]))
+    lens = rng.integers(-2, lmax + 1, size=batch)
+    lens[rng.random(batch) < 0.15] = 0
+    kv_dtype = E4M3 if rng.random() < 0.5 else FP16
+    layout = str(rng.choice(["contiguous", "interleaved", "head_major"]))
+    scales = (float(rng.uniform(0.5, 2.0)), float(rng.uniform(0.5, 1.5)))
+    splits = int(rng.choice([0, 0, 1, 2, 5]))
+    max_len = max(1, int(lens.max())) + int(rng.choice([0, 0, 17]))
+    case = inputs.decode_case(batch=batch, lens=lens, page_size=P, kv_dtype=kv_dtype,
+                              layout=layout, seed=i, num_q_heads=group * hkv,
+                              num_kv_heads=hkv, scales=scales, max_seq_len=max_len)
+    what = (f"sweep {i}: B{batch} lens<={lmax} P{P} hkv{hkv} group{group} "
+            f"{'e4m3' if kv_dtype == E4M3 else 'fp16'} {layout} splits{splits}")
+    return case, splits, what
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_random_configurations(pg, i):
+    """Each configuration through decode and through sparse prefill (rows as
+    sequences) against the oracle; empty and negative lengths give zeros."""
+    case, splits, what = _sweep_case(i)
+    print(what, flush=True)
+    ref = oracle.paged_gqa(**case.oracle_kwargs())
+    for prefill in (False, True):
+        got = _run(pg, case, prefill=prefill, num_splits=splits)
+        assert_parity(got, ref, what + (" prefill" if prefill else " decode"))
+        assert np.all(got[case.lens <= 0] == 0)
