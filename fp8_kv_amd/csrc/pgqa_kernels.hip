@@ -718,11 +718,16 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   }
 }
 
-// Merge the split partials of one (row, query head): one wave, each lane
-// owning 4 consecutive head dims.  Split s is weighted by 2^(lse_s - max lse);
-// a split with lse = -inf (no live token) has weight 0 and its stored output
-// is not used.  The lse values and the partial outputs of a chunk of 32
-// splits are loaded together, so a chunk costs about one memory round trip.
+// Merge the split partials of one (row, query head), each lane owning 4
+// consecutive head dims.  Split s is weighted by 2^(lse_s - max lse); a split
+// with lse = -inf (no live token) has weight 0 and its stored output is not
+// used.  The lse values and the partial outputs of a chunk of 32 splits are
+// loaded together, so a chunk costs about one memory round trip.  W = 1: one
+// wave takes the row's chunks in turn.  W > 1 (more than 32 splits): W waves
+// take chunks w, w + W, ... at once, each merging its own into (max, sum,
+// outputs, two chunks' loads in flight at once), and wave 0 combines the W
+// results in wave order through LDS, so a row of 256 splits costs one round
+// trip, not eight.
 //
 // Static layout (lens = nullptr): row r's partials are slots r*S .. r*S+S-1.
 // Balanced layout (a whole decode call, rows = (sequence b, query head h)):
@@ -730,9 +735,10 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
 // ((J / S) * hq + h) * S + J % S.  The first chunk is loaded at the static
 // slots while the lengths are in flight; it is loaded again only if the plan
 // is not the static one.
-__global__ __launch_bounds__(64) void merge_kernel(const float* lse_base, const float* o_base,
-                                                   int32_t splits, const int32_t* lens,
-                                                   int32_t n, int32_t hq_in, MergeParams p) {
+template <int W>
+__global__ __launch_bounds__(64 * W) void merge_kernel(const float* lse_base, const float* o_base,
+                                                       int32_t splits, const int32_t* lens,
+                                                       int32_t n, int32_t hq_in, MergeParams p) {
   p.lse = lse_base;  // leading arguments: preloaded into SGPRs
   p.o = o_base;
   p.splits = splits;
@@ -741,7 +747,7 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* lse_base, const 
   p.hq = hq_in;
   constexpr int kChunk = 32;
   const int S = p.splits;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int hq = p.lens ? p.hq : 1;
   const int row = blockIdx.x;
   const int b = row / hq;
@@ -817,6 +823,60 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* lse_base, const 
   int raw[kBalancePer];
   if (p.lens) balance_load(raw, p.lens, p.n, lane);
   int start = b * S, cnt = S;
+  if constexpr (W > 1) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (p.lens) {
+      const Balance B = balance_finish(raw, p.n, p.max_len, p.a_shift, lane);
+      if (!B.full) {
+        const int m = balance_units(B, p.n * S);
+        int st = 0, c = 0;
+        if (m > 0) balance_range(B, m, b, st, c);
+        start = st;
+        cnt = c;
+      }
+    }
+    // This wave's chunks c0, c0 + 32W, ..., two at a time: both chunks'
+    // loads are issued before either is merged, so a pair costs one round
+    // trip (with at most 4 waves a row of up to 256 splits is one pair).
+    for (int c0 = kChunk * wave; c0 < cnt; c0 += 2 * kChunk * W) {
+      const int c1 = c0 + kChunk * W;
+      float4 va[kChunk], vb[kChunk];
+      float la, lb = -__builtin_huge_valf();
+      load_chunk(va, la, start + c0, min(cnt - c0, kChunk), std::true_type{});
+      if (c1 < cnt) load_chunk(vb, lb, start + c1, min(cnt - c1, kChunk), std::true_type{});
+      combine(va, la);
+      if (c1 < cnt) combine(vb, lb);
+    }
+    __shared__ float4 s_acc[W][64];
+    __shared__ float s_m[W], s_den[W];
+    s_acc[wave][lane] = acc;
+    if (lane == 0) {
+      s_m[wave] = M;
+      s_den[wave] = den;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float mt = -__builtin_huge_valf();
+#pragma unroll
+    for (int w = 0; w < W; ++w) mt = fmaxf(mt, s_m[w]);
+    float dt = 0.f;
+    float4 at = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (mt != -__builtin_huge_valf()) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        if (s_m[w] == -__builtin_huge_valf()) continue;  // no live split in this wave
+        const float a = __builtin_amdgcn_exp2f(s_m[w] - mt);
+        const float4 x = s_acc[w][lane];
+        dt += a * s_den[w];
+        at.x += a * x.x;
+        at.y += a * x.y;
+        at.z += a * x.z;
+        at.w += a * x.w;
+      }
+    }
+    acc = at;
+    den = dt;
+  } else {
   float4 v[kChunk];
   float l;
   load_chunk(v, l, start, min(cnt, kChunk), std::true_type{});
@@ -844,6 +904,7 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* lse_base, const 
     float lw;
     load_chunk(w4, lw, start + c0, min(cnt - c0, kChunk), std::false_type{});
     combine(w4, lw);
+  }
   }
   const float scale = den > 0.f ? 1.f / den : 0.f;
   uint16_t* op = p.out + static_cast<int64_t>(row) * kHeadDim + 4 * lane;
@@ -909,9 +970,22 @@ hipError_t launch_attention(const AttnParams& p, bool fp8, hipStream_t stream) {
   }
 }
 
+template <int W>
+void launch_merge_w(const MergeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(merge_kernel<W>, dim3(static_cast<unsigned>(p.rows)), dim3(64 * W), 0, stream,
+                     p.lse, p.o, p.splits, p.lens, p.n, p.hq, p);
+}
+
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(p.rows)), dim3(64), 0, stream, p.lse,
-                     p.o, p.splits, p.lens, p.n, p.hq, p);
+  // Waves per row: one up to 32 splits, then one per 32 splits, at most 4
+  // (with 8 the 512-thread workgroup caps a wave at 256 VGPRs and the chunk
+  // registers spill; past 128 splits a wave takes two or more chunks).
+  if (p.splits <= 32)
+    launch_merge_w<1>(p, stream);
+  else if (p.splits <= 64)
+    launch_merge_w<2>(p, stream);
+  else
+    launch_merge_w<4>(p, stream);
   return hipGetLastError();
 }
 

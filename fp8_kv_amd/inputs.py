@@ -239,6 +239,23 @@ WORKLOADS = {
     "decode_b16_16k_e4m3_p128": dict(kind="decode", batch=16, lens=16384, page_size=128,
                                       kv_dtype=KV_E4M3, layout="contiguous", seed=0,
                                       scales="uniform"),
+    # The rest of the pages' batch-scaling grid (B1/B8/B16 x 1K/16K), in the
+    # benchmark's format (E4M3, page 128, scales ~ U[0.5, 2]).
+    "decode_b1_1k_e4m3_p128": dict(kind="decode", batch=1, lens=1024, page_size=128,
+                                    kv_dtype=KV_E4M3, layout="contiguous", seed=0,
+                                    scales="uniform"),
+    "decode_b8_1k_e4m3_p128": dict(kind="decode", batch=8, lens=1024, page_size=128,
+                                    kv_dtype=KV_E4M3, layout="contiguous", seed=0,
+                                    scales="uniform"),
+    "decode_b16_1k_e4m3_p128": dict(kind="decode", batch=16, lens=1024, page_size=128,
+                                     kv_dtype=KV_E4M3, layout="contiguous", seed=0,
+                                     scales="uniform"),
+    "decode_b1_16k_e4m3_p128": dict(kind="decode", batch=1, lens=16384, page_size=128,
+                                     kv_dtype=KV_E4M3, layout="contiguous", seed=0,
+                                     scales="uniform"),
+    "decode_b8_16k_e4m3_p128": dict(kind="decode", batch=8, lens=16384, page_size=128,
+                                     kv_dtype=KV_E4M3, layout="contiguous", seed=0,
+                                     scales="uniform"),
     "decode_ragged_b16_16k_p256": dict(kind="decode", batch=16, lens=("uniform", 1, 16384),
                                         page_size=256, max_seq_len=16384, seed=0),
     "prefill_sparse_4096x2051_p4": dict(kind="prefill", rows=4096, selected_blocks=512,

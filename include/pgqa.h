@@ -123,7 +123,8 @@ int32_t paged_gqa_num_splits(int32_t n, int32_t num_kv_heads, int32_t max_seq_le
  * num_q_heads: group * num_kv_heads with 1 <= group <= 16 (6 in the pages).
  * head_dim   : must be 256.
  * sm_scale   : softmax scale applied to q.K (finite).
- * num_splits : number of key-range splits per (sequence, kv head), 0 = auto;
+ * num_splits : number of key-range splits per (sequence, kv head), 0 = auto
+ *              (about one workgroup per compute unit, at most 128 splits);
  *              capped at 256 and at one split per 64 tokens (query the
  *              effective count with paged_gqa_num_splits).
  *              With more than one split the call writes split partials into

@@ -589,3 +589,37 @@ def test_random_configurations(pg, i):
         got = _run(pg, case, prefill=prefill, num_splits=splits)
         assert_parity(got, ref, what + (" prefill" if prefill else " decode"))
         assert np.all(got[case.lens <= 0] == 0)
+
+
+@pytest.mark.parametrize("splits", [32, 33, 64, 65, 128, 200, 256, 0])
+def test_many_splits_merge(pg, splits):
+    """Split counts on both sides of each merge width (one wave up to 32
+    splits, then 2 and 4 waves per row): a whole call, and decode_partial +
+    merge_partials, against the oracle; the two agree bit for bit."""
+    import torch
+
+    case = inputs.decode_case(batch=2, lens=[16384, 16384], page_size=128, kv_dtype=E4M3,
+                              seed=79, scales="uniform")
+    ref = oracle.paged_gqa(**case.oracle_kwargs())
+    q, pool, table, lens = pg.device_case(case)
+    n, hq, _ = q.shape
+    S = pg.paged_gqa_num_splits(n, 1, case.max_seq_len, splits)
+    print(f"many splits: requested {splits} -> {S}", flush=True)
+    whole = _run(pg, case, num_splits=splits)
+    assert_parity(whole, ref, f"splits {S} whole call")
+    po = torch.empty((n, hq, S, 256), dtype=torch.float32, device="cuda")
+    pl = torch.empty((n, hq, S), dtype=torch.float32, device="cuda")
+    pg.paged_gqa_decode_partial(q, pool, table, lens, case.max_seq_len, case.sm_scale, po, pl,
+                                num_splits=splits)
+    merged = torch.empty_like(q)
+    pg.paged_gqa_merge_partials(po, pl, merged)
+    torch.cuda.synchronize()
+    assert np.array_equal(merged.cpu().numpy().view(np.uint16), whole.view(np.uint16))
+
+
+def test_b1_long_context_auto_splits(pg):
+    """One 16K sequence: the automatic plan takes its largest split count
+    (more than 64, so the merge runs four waves per row)."""
+    case = inputs.workload_case("decode_b1_16k_e4m3_p128")
+    assert pg.paged_gqa_num_splits(1, 1, case.max_seq_len, 0) > 64
+    _check(pg, case, "b1 16k auto splits")
