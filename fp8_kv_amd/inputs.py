@@ -261,6 +261,10 @@ WORKLOADS = {
     "prefill_sparse_4096x2051_p4": dict(kind="prefill", rows=4096, selected_blocks=512,
                                          tail=3, pool_blocks=65536, layout="interleaved",
                                          seed=0),
+    # The same shape over an FP8-E4M3 pool (scales ~ U[0.5, 2]).
+    "prefill_sparse_4096x2051_p4_e4m3": dict(kind="prefill", rows=4096, selected_blocks=512,
+                                              tail=3, pool_blocks=65536, layout="interleaved",
+                                              seed=0, kv_dtype=KV_E4M3, scales="uniform"),
     # The same shape with groups of 32 consecutive rows sharing a selection.
     "prefill_sparse_4096x2051_p4_shared32": dict(kind="prefill", rows=4096,
                                                   selected_blocks=512, tail=3,

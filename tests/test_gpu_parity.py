@@ -80,14 +80,16 @@ def test_workload_ragged(pg, kv_dtype, layout):
     _check(pg, case, f"ragged {kv_dtype} {layout}")
 
 
-def test_workload_sparse_prefill_sampled(pg):
-    case = inputs.workload_case("prefill_sparse_4096x2051_p4")
+@pytest.mark.parametrize("name", ["prefill_sparse_4096x2051_p4",
+                                  "prefill_sparse_4096x2051_p4_e4m3"])
+def test_workload_sparse_prefill_sampled(pg, name):
+    case = inputs.workload_case(name)
     rng = np.random.default_rng(1)
     ids = np.unique(np.concatenate([[0, 1, case.n - 1],
                                     rng.choice(case.n, 509, replace=False)])).astype(np.int32)
     got = _run(pg, case, prefill=True)
     ref = oracle.paged_gqa(**case.oracle_kwargs(), seq_ids=ids)
-    assert_parity(got[ids], ref, "prefill 4096x2051 sampled rows")
+    assert_parity(got[ids], ref, f"{name} sampled rows")
     assert np.isfinite(got).all()
 
 
