@@ -303,3 +303,17 @@ def test_stream_read_library_validation():
     assert f(FAKE + 8, 64, None, 0, 4, 1, FAKE, None) == -3      # alignment
     assert f(FAKE, 64, FAKE + 4, 16, 4, 1, FAKE, None) == -3
     assert f(FAKE, 64, None, 0, 4, 1, FAKE + 8, None) == -3
+
+
+def test_explicit_split_counts(lib):
+    """A requested split count becomes a chunk length rounded up to a
+    multiple of 64 tokens, then the count that chunk gives; at most 256 and
+    one split per 64 tokens (no device query for explicit counts)."""
+    f = lib.paged_gqa_num_splits
+    assert f(2, 1, 16384, 300) == 256
+    assert f(2, 1, 16384, 200) == 128
+    assert f(2, 1, 16384, 45) == 43
+    assert f(2, 1, 16384, 100) == 86
+    assert f(2, 1, 12000, 190) == 188
+    assert f(1, 1, 64, 5) == 1
+    assert f(1, 1, 100, 50) == 2

@@ -593,26 +593,33 @@ def test_random_configurations(pg, i):
         assert np.all(got[case.lens <= 0] == 0)
 
 
-@pytest.mark.parametrize("splits", [32, 33, 64, 65, 128, 200, 256, 0])
-def test_many_splits_merge(pg, splits):
-    """Split counts on both sides of each merge width (one wave up to 32
-    splits, then 2 and 4 waves per row): a whole call, and decode_partial +
-    merge_partials, against the oracle; the two agree bit for bit."""
+@pytest.mark.parametrize("length,requested,S", [
+    (16384, 32, 32), (16384, 45, 43), (16384, 64, 64), (16384, 100, 86), (16384, 128, 128),
+    (12000, 190, 188), (16384, 256, 256), (16384, 0, None)])
+def test_many_splits_merge(pg, length, requested, S):
+    """Effective split counts (a request is rounded through a chunk length
+    that is a multiple of 64 tokens) on each merge width: one wave up to 32
+    splits, two waves up to 64, four beyond, with partial last chunks (43,
+    86, 188) and two chunks per wave (188, 256).  A whole call and
+    decode_partial + merge_partials against the oracle; the two agree bit for
+    bit."""
     import torch
 
-    case = inputs.decode_case(batch=2, lens=[16384, 16384], page_size=128, kv_dtype=E4M3,
+    case = inputs.decode_case(batch=2, lens=[length, length], page_size=128, kv_dtype=E4M3,
                               seed=79, scales="uniform")
     ref = oracle.paged_gqa(**case.oracle_kwargs())
     q, pool, table, lens = pg.device_case(case)
     n, hq, _ = q.shape
-    S = pg.paged_gqa_num_splits(n, 1, case.max_seq_len, splits)
-    print(f"many splits: requested {splits} -> {S}", flush=True)
-    whole = _run(pg, case, num_splits=splits)
-    assert_parity(whole, ref, f"splits {S} whole call")
-    po = torch.empty((n, hq, S, 256), dtype=torch.float32, device="cuda")
-    pl = torch.empty((n, hq, S), dtype=torch.float32, device="cuda")
+    got_S = pg.paged_gqa_num_splits(n, 1, case.max_seq_len, requested)
+    print(f"many splits: L {length} requested {requested} -> {got_S}", flush=True)
+    if S is not None:
+        assert got_S == S
+    whole = _run(pg, case, num_splits=requested)
+    assert_parity(whole, ref, f"splits {got_S} whole call")
+    po = torch.empty((n, hq, got_S, 256), dtype=torch.float32, device="cuda")
+    pl = torch.empty((n, hq, got_S), dtype=torch.float32, device="cuda")
     pg.paged_gqa_decode_partial(q, pool, table, lens, case.max_seq_len, case.sm_scale, po, pl,
-                                num_splits=splits)
+                                num_splits=requested)
     merged = torch.empty_like(q)
     pg.paged_gqa_merge_partials(po, pl, merged)
     torch.cuda.synchronize()
