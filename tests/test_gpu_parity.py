@@ -632,3 +632,55 @@ def test_b1_long_context_auto_splits(pg):
     case = inputs.workload_case("decode_b1_16k_e4m3_p128")
     assert pg.paged_gqa_num_splits(1, 1, case.max_seq_len, 0) > 64
     _check(pg, case, "b1 16k auto splits")
+
+
+def test_two_streams_at_once(pg):
+    """The library keeps no per-call state: calls launched on two streams
+    without synchronisation between them (decode, sparse prefill and masking
+    interleaved) give the same bits as the same calls one after another."""
+    import torch
+
+    dec = inputs.decode_case(batch=4, lens=[5000, 17, 3000, 0], page_size=64, kv_dtype=E4M3,
+                             seed=81, scales="uniform")
+    pre = inputs.sparse_prefill_case(rows=64, selected_blocks=40, tail=2, pool_blocks=1024,
+                                     seed=82)
+    sam = inputs.sampler_case(rows=4, vocab=50_000, k=[20, 1, 256, 7], p=0.9, seed=83)
+    d = pg.device_case(dec)
+    r = pg.device_case(pre)
+    z = torch.from_numpy(sam.logits).cuda()
+    k = torch.from_numpy(np.array(sam.k, np.int32)).cuda()
+    pp = torch.from_numpy(np.array(sam.p, np.float32)).cuda()
+
+    def work(stream, outs):
+        wsb = pg.paged_gqa_workspace_bytes(4, 6, 1, dec.max_seq_len, 0)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        wsb2 = pg.paged_gqa_workspace_bytes(pre.n, 6, 1, pre.max_seq_len, 0)
+        ws2 = torch.empty(max(wsb2, 16), dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            pg.paged_gqa_decode(d[0], d[1], d[2], d[3], dec.max_seq_len, dec.sm_scale, outs[0],
+                                workspace=ws, stream=stream)
+            pg.paged_gqa_prefill_sparse(r[0], r[1], r[2], r[3], pre.max_seq_len, pre.sm_scale,
+                                        outs[1], workspace=ws2, stream=stream)
+            pg.sampler_topk_topp_mask(z, k, pp, out=outs[2], stream=stream)
+
+    def fresh():
+        return [torch.empty_like(d[0]), torch.empty_like(r[0]), torch.empty_like(z)]
+
+    ref = fresh()
+    work(torch.cuda.current_stream(), ref)
+    torch.cuda.synchronize()
+    a, b = fresh(), fresh()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s1):
+        work(s1, a)
+    with torch.cuda.stream(s2):
+        work(s2, b)
+    torch.cuda.synchronize()
+    for x, y, w in zip(a, b, ref):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.float16 else x.view(torch.int32),
+                           w.view(torch.int16) if w.dtype == torch.float16 else w.view(torch.int32))
+        assert torch.equal(y.view(torch.int16) if y.dtype == torch.float16 else y.view(torch.int32),
+                           w.view(torch.int16) if w.dtype == torch.float16 else w.view(torch.int32))
+    assert_parity(a[0].cpu().numpy(), oracle.paged_gqa(**dec.oracle_kwargs()), "two streams")
