@@ -8,14 +8,14 @@ replicated into R separate device copies and the steps rotate through them,
 so consecutive calls cannot be served from the 256 MB last-level cache.
 
 Prints ONE JSON line.  `value` is KV-read GB/s: algorithmic KV bytes per call
-(every live token's K and V row read once) divided by the average call time
-measured with HIP events on the stream the kernels run on.  `roofline` uses
-the dominant kernel alone (the attention kernel, timed the same way through
-paged_gqa_decode_partial with the same split plan); the whole call adds the
-split merge.  Beside them: `repeat` (the timed batch and four more of the same
-size), `warm` (one pool reused every call, so not an HBM rate) and, for
-decode, `read_ceiling` (a plain streaming read of the same number of bytes
-from the same rotated pools: the rate those bytes can reach here).
+(every live token's K and V row read once) divided by the call time, the
+median of five batches of exactly K calls, each batch's average measured with
+HIP events on the stream the kernels run on.  `roofline` uses the dominant
+kernel alone (timed the same way) when the call has more than one.  Beside
+them: `repeat` (the five batches), `warm` (one pool reused every call, so not
+an HBM rate) and, for decode, `read_ceiling` (a plain streaming read of the
+same number of bytes from the same rotated pools: the rate those bytes can
+reach here).
 """
 from __future__ import annotations
 
@@ -313,13 +313,18 @@ def bench_sampler(args) -> int:
 def time_batches(step, steps: int, warmup: int, R: int, use_graph: bool,
                  batches: int = 1) -> list[float]:
     """Average milliseconds per step over exactly `steps` steps, timed with HIP
-    events on the stream the kernels run on.  With use_graph the steps are
-    captured into one HIP graph (up to kGraphSteps of them, cycling through the
-    R pools, replayed as often as needed, the remainder eager), as a serving
-    loop captures a whole decode step, so neither Python's per-call overhead
-    nor graph-launch boundaries leave the GPU idle between steps.  Returns
-    one average per batch; every batch is exactly `steps` steps with its own
-    events."""
+    events on the stream the kernels run on; one average per batch.
+
+    With use_graph the steps are captured into one HIP graph (up to
+    kGraphSteps of them, cycling through the R pools, replayed as often as
+    needed, the remainder eager), as a serving loop captures a whole decode
+    step, so neither Python's per-call overhead nor graph-launch boundaries
+    leave the GPU idle between steps.  Before each timed batch one untimed
+    replay of the same graph is queued without waiting for it: the GPU runs
+    it while the host submits the timed replays, so the first timed step
+    starts as soon as that untimed replay ends, not when the host has finished
+    submitting (with 20-step graphs the host's submission latency otherwise
+    lands inside the events, spread over only 20 calls)."""
     import torch
 
     kGraphSteps = 512
@@ -351,6 +356,8 @@ def time_batches(step, steps: int, warmup: int, R: int, use_graph: bool,
     out = []
     for _ in range(batches):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if use_graph and G > 0:
+            replay()  # untimed: keeps the GPU busy while the timed steps are queued
         e0.record(cur)
         for _ in range(steps // per_replay):
             replay()
@@ -362,9 +369,11 @@ def time_batches(step, steps: int, warmup: int, R: int, use_graph: bool,
     return out
 
 
-def time_steps(step, steps: int, warmup: int, R: int, use_graph: bool) -> float:
-    """Average milliseconds per step over exactly `steps` steps (one batch)."""
-    return time_batches(step, steps, warmup, R, use_graph)[0]
+def time_steps(step, steps: int, warmup: int, R: int, use_graph: bool,
+               batches: int = 3) -> float:
+    """Median over `batches` batches of the average milliseconds per step,
+    each batch exactly `steps` steps."""
+    return float(np.median(time_batches(step, steps, warmup, R, use_graph, batches)))
 
 
 def read_ceiling(pools, kv_bytes: int, steps: int, warmup: int, use_graph: bool) -> dict:
@@ -471,7 +480,7 @@ def main() -> int:
                                       num_splits=args.num_splits)
 
     batches = time_batches(call, args.steps, args.warmup, R, not args.eager, batches=5)
-    ms = batches[0]  # the timed K steps; the four batches after it show the spread
+    ms = float(np.median(batches))  # five batches of exactly K steps each: their median
     # decode_partial runs the attention kernel of a whole call only when both
     # use the static split plan: decode (not prefill) with every length at
     # max_seq_len, or more sequences than the balanced plan covers.
@@ -523,7 +532,9 @@ def main() -> int:
     }
     result["repeat"] = {"batches": len(batches), "steps_each": args.steps,
                         "us_per_call": [round(b * 1e3, 3) for b in batches],
-                        "median_us": round(float(np.median(batches)) * 1e3, 3)}
+                        "median_us": round(ms * 1e3, 3),
+                        "first_us": round(batches[0] * 1e3, 3),
+                        "spread_us": round((max(batches) - min(batches)) * 1e3, 3)}
     if R > 1:
         warm_ms = time_steps(lambda i: call(0), args.steps, args.warmup, 1, not args.eager)
         result["warm"] = {

@@ -20,15 +20,10 @@ using pgqa::kHeadDim;
 using pgqa::kMaxGroup;
 using pgqa::kTile;
 
-// Tuning constants (compile-time): waves per workgroup and resident waves
-// per compute unit the split plan aims for.
-#ifndef PGQA_WAVES_PER_WG
-#define PGQA_WAVES_PER_WG 4
-#endif
-#ifndef PGQA_WAVES_PER_CU
-#define PGQA_WAVES_PER_CU 4
-#endif
-constexpr int kWaves = PGQA_WAVES_PER_WG;
+// Split planning: waves per workgroup (fixed by the kernels) and resident
+// waves per compute unit the automatic split count aims for.
+constexpr int kWaves = pgqa::kWavesPerWg;
+constexpr int kWavesPerCu = 4;
 // Upper bound on splits (the merge reads every partial of a head).
 constexpr int64_t kMaxSplits = 256;
 // Upper bound on the automatic choice: past it the merge's reads of the
@@ -36,14 +31,11 @@ constexpr int64_t kMaxSplits = 256;
 // E4M3: 11.5 us per call at 128 splits, 14.0 at 256).
 constexpr int64_t kAutoMaxSplits = 128;
 constexpr int kChunkAlign = kTile * kWaves;  // split length granularity
-constexpr int kChunkAlignShift = kWaves == 4 ? 6 : 7;
-static_assert(kWaves == 4 || kWaves == 8, "workgroups have 4 or 8 waves");
+constexpr int kChunkAlignShift = 6;
 static_assert(kChunkAlign == 1 << kChunkAlignShift, "granularity is a power of two");
 // Rows up to this length, when there are enough of them to give every compute
 // unit a workgroup of kWaves rows, run one row per wave.
-#ifndef PGQA_ROW_PER_WAVE_MAX_LEN
-#define PGQA_ROW_PER_WAVE_MAX_LEN 4096
-#endif
+constexpr int kRowPerWaveMaxLen = 4096;
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
@@ -73,7 +65,7 @@ struct SplitPlan {
   int32_t chunk;
 };
 
-// Key-range splits: aim for PGQA_WAVES_PER_CU resident waves per compute
+// Key-range splits: aim for kWavesPerCu resident waves per compute
 // unit, never fewer than kChunkAlign tokens (one tile per wave) per split.
 SplitPlan plan_splits(int64_t groups, int32_t max_len, int32_t requested, int cus) {
   const int64_t len = max_len > 0 ? max_len : 1;
@@ -83,7 +75,7 @@ SplitPlan plan_splits(int64_t groups, int32_t max_len, int32_t requested, int cu
     s = requested;
   } else {
     const int64_t target_wgs =
-        static_cast<int64_t>(cus > 0 ? cus : 256) * PGQA_WAVES_PER_CU / kWaves;
+        static_cast<int64_t>(cus > 0 ? cus : 256) * kWavesPerCu / kWaves;
     s = ceil_div(target_wgs, groups > 0 ? groups : 1);
     if (s > kAutoMaxSplits) s = kAutoMaxSplits;
   }
@@ -172,7 +164,6 @@ pgqa::AttnParams make_params(const void* q, const pgqa_kv_pool* kv, const int32_
   p.v_scale = fp8 ? kv->v_scale : 1.0f;
   p.splits = plan.splits;
   p.chunk = plan.chunk;
-  p.waves = kWaves;
   return p;
 }
 
@@ -213,7 +204,7 @@ int run_attention(const void* q, const pgqa_kv_pool* kv, const int32_t* table, i
     // Unequal lengths: the kernels spread the live tokens over all n*S
     // workgroup slots of a kv head (the partial layout stays internal).
     if (n <= pgqa::kBalanceMaxSeqs) p.balance_n = n;
-  } else if (max_len <= PGQA_ROW_PER_WAVE_MAX_LEN) {
+  } else if (max_len <= kRowPerWaveMaxLen) {
     // One split and many rows: a workgroup of kWaves rows pays its launch
     // and ramp once for all of them.
     const int cus = current_cu_count();
@@ -294,7 +285,7 @@ int paged_gqa_decode_partial(const void* q, const pgqa_kv_pool* kv, const int32_
                          num_kv_heads, head_dim, sm_scale, num_splits, part_o);
   if (rc != PGQA_OK || batch == 0) return rc;
   if (!part_lse) return PGQA_ERR_NULL;
-  if (!aligned16(part_lse)) return PGQA_ERR_LAYOUT;
+  if (reinterpret_cast<uintptr_t>(part_lse) & 3u) return PGQA_ERR_LAYOUT;
   SplitPlan plan;
   rc = plan_call(batch, num_kv_heads, max_seq_len, num_splits, &plan);
   if (rc != PGQA_OK) return rc;
@@ -315,7 +306,8 @@ int paged_gqa_merge_partials(const float* part_o, const float* part_lse, int32_t
   if (head_dim != kHeadDim || rows < 0 || splits < 1) return PGQA_ERR_SHAPE;
   if (rows == 0) return PGQA_OK;
   if (!part_o || !part_lse || !out) return PGQA_ERR_NULL;
-  if (!aligned16(part_o) || !aligned16(out)) return PGQA_ERR_LAYOUT;
+  if (!aligned16(part_o) || !aligned16(out) || (reinterpret_cast<uintptr_t>(part_lse) & 3u))
+    return PGQA_ERR_LAYOUT;
   pgqa::MergeParams m{part_o, part_lse, rows, splits, static_cast<uint16_t*>(out)};
   return pgqa::launch_merge(m, static_cast<hipStream_t>(stream)) == hipSuccess ? PGQA_OK
                                                                                 : PGQA_ERR_HIP;

@@ -9,7 +9,7 @@ namespace pgqa {
 
 constexpr int kHeadDim = 256;   // head dimension the kernels are built for
 constexpr int kTile = 16;       // tokens per wave tile (one MFMA M/K block)
-constexpr int kMaxWaves = 8;    // waves per workgroup (4 or 8), each on its own tiles
+constexpr int kWavesPerWg = 4;  // waves per attention workgroup, each on its own tiles
 constexpr int kMaxGroup = 16;   // query heads per kv head (MFMA N = 16)
 constexpr int kBalanceMaxSeqs = 512;  // sequences a balanced (ragged) plan covers
 
@@ -36,7 +36,6 @@ struct AttnParams {
   float v_scale;           // 1 for FP16
   int32_t splits;          // key-range splits per (sequence, kv head)
   int32_t chunk;           // tokens per split, multiple of kTile * waves
-  int32_t waves;           // waves per workgroup: 4 or 8
   int32_t balance_n;       // n > 0: spread unequal lengths over the n*splits slots
                            // (split partials only, n <= kBalanceMaxSeqs); 0: static
   bool partials;           // write split partials (ws_o, ws_lse) instead of out

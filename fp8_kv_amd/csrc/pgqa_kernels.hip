@@ -11,7 +11,7 @@
 //     clamped to their live length, invalid rows inert, page ids of a tile
 //     staged ahead of its loads.
 //
-// Work decomposition.  One workgroup of NW (4 or 8) waves owns one (sequence or row
+// Work decomposition.  One workgroup of NW (kWavesPerWg) waves owns one (sequence or row
 // b, kv head g, split s): the tokens [s*chunk, min((s+1)*chunk, L_b)).  Wave
 // w takes the 16-token tiles w, w+4, w+8, ... of that range and keeps its own
 // online-softmax state; the four states are merged through LDS at the end.
@@ -46,6 +46,7 @@
 //     16*m + j (FP8) or 128*(j/8) + 8*m + j%8 (FP16).
 #include <type_traits>
 
+#include "launch_util.h"
 #include "pgqa_internal.h"
 
 namespace pgqa {
@@ -61,13 +62,11 @@ typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 constexpr int kLdsRow = kHeadDim + 4;  // padded fp32 row of the merge buffer
 
 // Tile buffers per wave (tiles in flight while one is computed: depth - 1).
-#ifndef PGQA_PIPELINE_DEPTH
-#define PGQA_PIPELINE_DEPTH 2
-#endif
+// Depth 3 was measured slower at every length (more VGPRs, fewer waves in
+// flight per CU), as were 8-wave workgroups.
+constexpr int kPipelineDepth = 2;
 // Tiles by which page-table entries are loaded ahead of their K/V loads.
-#ifndef PGQA_PAGE_LOOKAHEAD
-#define PGQA_PAGE_LOOKAHEAD 1
-#endif
+constexpr int kPageLookahead = 1;
 
 // ------------------------------------------------------------ ragged balance
 // A whole decode call over sequences of unequal length spreads the live tokens
@@ -922,8 +921,8 @@ __global__ void e4m3_table_kernel(float* out) {
 
 template <bool FP8, int NW, bool NT, bool RW>
 hipError_t launch(const AttnParams& p, hipStream_t stream) {
-  constexpr int PD = PGQA_PIPELINE_DEPTH;
-  constexpr int PL = PGQA_PAGE_LOOKAHEAD;
+  constexpr int PD = kPipelineDepth;
+  constexpr int PL = kPageLookahead;
   const size_t lds = RW ? 0 : attention_lds_bytes(p.group, NW);
   if (lds > 65536) {
     // Merge buffers beyond the default 64 KiB dynamic LDS limit need the
@@ -936,10 +935,9 @@ hipError_t launch(const AttnParams& p, hipStream_t stream) {
   }
   const int64_t rows = static_cast<int64_t>(p.n) * p.hkv;
   const dim3 grid(static_cast<unsigned>(RW ? (rows + NW - 1) / NW : p.splits * rows));
-  hipLaunchKernelGGL((attention_kernel<FP8, NW, PD, PL, NT, RW>), grid, dim3(64 * NW), lds, stream,
-                     p.table, p.lens, p.max_pages, p.max_len, p.chunk, p.splits, p.hkv,
-                     p.page_size, p.inv_page_size, p.balance_n, p);
-  return hipGetLastError();
+  return pgqa_launch::launch(attention_kernel<FP8, NW, PD, PL, NT, RW>, grid, dim3(64 * NW), lds,
+                             stream, p.table, p.lens, p.max_pages, p.max_len, p.chunk, p.splits,
+                             p.hkv, p.page_size, p.inv_page_size, p.balance_n, p);
 }
 
 template <bool FP8, int NW, bool NT>
@@ -956,42 +954,29 @@ size_t attention_lds_bytes(int group, int waves) {
 }
 
 hipError_t launch_attention(const AttnParams& p, bool fp8, hipStream_t stream) {
-  if (p.stream_kv) {
-    switch (p.waves) {
-      case 4: return fp8 ? launch_rw<true, 4, true>(p, stream) : launch_rw<false, 4, true>(p, stream);
-      case 8: return fp8 ? launch_rw<true, 8, true>(p, stream) : launch_rw<false, 8, true>(p, stream);
-      default: return hipErrorInvalidValue;
-    }
-  }
-  switch (p.waves) {
-    case 4: return fp8 ? launch_rw<true, 4, false>(p, stream) : launch_rw<false, 4, false>(p, stream);
-    case 8: return fp8 ? launch_rw<true, 8, false>(p, stream) : launch_rw<false, 8, false>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
+  constexpr int NW = kWavesPerWg;
+  if (p.stream_kv)
+    return fp8 ? launch_rw<true, NW, true>(p, stream) : launch_rw<false, NW, true>(p, stream);
+  return fp8 ? launch_rw<true, NW, false>(p, stream) : launch_rw<false, NW, false>(p, stream);
 }
 
 template <int W>
-void launch_merge_w(const MergeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(merge_kernel<W>, dim3(static_cast<unsigned>(p.rows)), dim3(64 * W), 0, stream,
-                     p.lse, p.o, p.splits, p.lens, p.n, p.hq, p);
+hipError_t launch_merge_w(const MergeParams& p, hipStream_t stream) {
+  return pgqa_launch::launch(merge_kernel<W>, dim3(static_cast<unsigned>(p.rows)), dim3(64 * W), 0,
+                             stream, p.lse, p.o, p.splits, p.lens, p.n, p.hq, p);
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   // Waves per row: one up to 32 splits, then one per 32 splits, at most 4
   // (with 8 the 512-thread workgroup caps a wave at 256 VGPRs and the chunk
   // registers spill; past 128 splits a wave takes two or more chunks).
-  if (p.splits <= 32)
-    launch_merge_w<1>(p, stream);
-  else if (p.splits <= 64)
-    launch_merge_w<2>(p, stream);
-  else
-    launch_merge_w<4>(p, stream);
-  return hipGetLastError();
+  if (p.splits <= 32) return launch_merge_w<1>(p, stream);
+  if (p.splits <= 64) return launch_merge_w<2>(p, stream);
+  return launch_merge_w<4>(p, stream);
 }
 
 hipError_t launch_e4m3_table(float* out256, hipStream_t stream) {
-  hipLaunchKernelGGL(e4m3_table_kernel, dim3(1), dim3(256), 0, stream, out256);
-  return hipGetLastError();
+  return pgqa_launch::launch(e4m3_table_kernel, dim3(1), dim3(256), 0, stream, out256);
 }
 
 }  // namespace pgqa

@@ -48,6 +48,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch_util.h"
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -509,8 +510,8 @@ hipError_t launch_e(const Page4Params& p, int32_t hash_log2, hipStream_t stream)
     if (raised != hipSuccess) return raised;
   }
   const unsigned groups = static_cast<unsigned>((p.rows + W - 1) / W);
-  hipLaunchKernelGGL((page4_kernel<E, W>), dim3(groups), dim3(64 * W), lds, stream, p, hash_log2);
-  return hipGetLastError();
+  return pgqa_launch::launch(page4_kernel<E, W>, dim3(groups), dim3(64 * W), lds, stream, p,
+                             hash_log2);
 }
 
 }  // namespace

@@ -47,6 +47,7 @@
 
 #include <type_traits>
 
+#include "launch_util.h"
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -514,10 +515,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
 template <int ITEMS>
 hipError_t launch_items(const TopkParams& p, bool vec, hipStream_t stream) {
   if (vec)
-    hipLaunchKernelGGL((topk_kernel<ITEMS, true>), dim3(p.rows), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((topk_kernel<ITEMS, false>), dim3(p.rows), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+    return pgqa_launch::launch(topk_kernel<ITEMS, true>, dim3(p.rows), dim3(kThreads), 0, stream,
+                               p);
+  return pgqa_launch::launch(topk_kernel<ITEMS, false>, dim3(p.rows), dim3(kThreads), 0, stream,
+                             p);
 }
 
 }  // namespace

@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch_util.h"
 #include "sampler_internal.h"
 
 namespace sampler {
@@ -579,7 +580,9 @@ hipError_t launch_mask(const MaskParams& p, hipStream_t stream) {
   const size_t lds1 = sizeof(uint64_t) * pow2;
   const dim3 grid1(p.n_chunks, p.rows);
   if (p.chunk <= 16 * kThreads) {
-    hipLaunchKernelGGL(chunk_top_kernel<16>, grid1, dim3(kThreads), lds1, stream, p);
+    const hipError_t e1 =
+        pgqa_launch::launch(chunk_top_kernel<16>, grid1, dim3(kThreads), lds1, stream, p);
+    if (e1 != hipSuccess) return e1;  // the cut kernel would read an unfilled workspace
   } else {
     if (lds1 > 65536 - 64) {
       static const hipError_t raised = hipFuncSetAttribute(
@@ -588,8 +591,9 @@ hipError_t launch_mask(const MaskParams& p, hipStream_t stream) {
           static_cast<int>(sizeof(uint64_t) * kMaxChunk));
       if (raised != hipSuccess) return raised;
     }
-    hipLaunchKernelGGL(chunk_top_kernel<kMaxChunk / kThreads>, grid1, dim3(kThreads), lds1, stream,
-                       p);
+    const hipError_t e1 = pgqa_launch::launch(chunk_top_kernel<kMaxChunk / kThreads>, grid1,
+                                              dim3(kThreads), lds1, stream, p);
+    if (e1 != hipSuccess) return e1;
   }
   const size_t lds = sizeof(uint64_t) * static_cast<size_t>(p.n_chunks) * p.k_max;
   if (lds > 65536) {
@@ -598,8 +602,7 @@ hipError_t launch_mask(const MaskParams& p, hipStream_t stream) {
         static_cast<int>(sizeof(uint64_t) * kMaxChunks * kMaxK));
     if (raised != hipSuccess) return raised;
   }
-  hipLaunchKernelGGL(cut_kernel, dim3(p.rows), dim3(64), lds, stream, p);
-  return hipGetLastError();
+  return pgqa_launch::launch(cut_kernel, dim3(p.rows), dim3(64), lds, stream, p);
 }
 
 }  // namespace sampler

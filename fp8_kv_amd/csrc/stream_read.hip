@@ -22,6 +22,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "launch_util.h"
+
 namespace {
 
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
@@ -108,13 +110,13 @@ int stream_read(const void* a, size_t a_bytes, const void* b, size_t b_bytes, in
   const auto* pb = static_cast<const u4_t*>(b);
   auto* ps = static_cast<u4_t*>(sink);
   const auto st = static_cast<hipStream_t>(stream);
-  if (nontemporal)
-    hipLaunchKernelGGL(stream_read_kernel<true>, dim3(blocks), dim3(kThreads), 0, st, pa, na, pb,
-                       per_block, n, ps);
-  else
-    hipLaunchKernelGGL(stream_read_kernel<false>, dim3(blocks), dim3(kThreads), 0, st, pa, na,
-                       pb, per_block, n, ps);
-  return hipGetLastError() == hipSuccess ? 0 : -4;
+  const hipError_t e =
+      nontemporal
+          ? pgqa_launch::launch(stream_read_kernel<true>, dim3(blocks), dim3(kThreads), 0, st, pa,
+                                na, pb, per_block, n, ps)
+          : pgqa_launch::launch(stream_read_kernel<false>, dim3(blocks), dim3(kThreads), 0, st,
+                                pa, na, pb, per_block, n, ps);
+  return e == hipSuccess ? 0 : -4;
 }
 
 }  // extern "C"

@@ -26,7 +26,11 @@
  *     = the default stream).  Work is enqueued asynchronously: a return of
  *     PGQA_OK means the launch was accepted, and device faults surface at the
  *     caller's next synchronisation, as usual in HIP.
- *   - On any error code nothing is launched and no output is written.
+ *   - On an argument error code nothing is launched and no output is written.
+ *     PGQA_ERR_HIP means the HIP runtime refused a launch (the status of that
+ *     launch itself, not an error left over from earlier HIP calls); a call
+ *     that launches two kernels never launches the second after the first
+ *     was refused.
  *   - Thread-safe and stateless apart from a per-device cache of the compute
  *     unit count.  Calls may be captured into HIP graphs (no allocation, no
  *     synchronisation, no memset inside).
@@ -177,9 +181,9 @@ int paged_gqa_prefill_sparse(const void* q, const pgqa_kv_pool* kv, const int32_
  * chunk C = ceil(max_seq_len / S) rounded up to a multiple of 64, and writes
  *   part_o  : fp32 [batch][num_q_heads][S][256], 16-byte aligned: the
  *             split's softmax-weighted mean of V (v_scale applied);
- *   part_lse: fp32 [batch][num_q_heads][S]: log2(sum_t exp(z_t)) over the
- *             split's tokens, or -inf for a split with no live token (its
- *             part_o is then not written).
+ *   part_lse: fp32 [batch][num_q_heads][S], 4-byte aligned:
+ *             log2(sum_t exp(z_t)) over the split's tokens, or -inf for a
+ *             split with no live token (its part_o is then not written).
  * Both buffers are caller-allocated device memory of at least the sizes above.
  */
 int paged_gqa_decode_partial(const void* q, const pgqa_kv_pool* kv, const int32_t* page_table,
@@ -196,7 +200,7 @@ int paged_gqa_decode_partial(const void* q, const pgqa_kv_pool* kv, const int32_
  * 2^(lse_s - M), M = max_s lse_s; splits with lse = -inf are skipped and a
  * row whose splits are all -inf is zero.  part_o fp32 [rows][splits][256]
  * and out fp16 [rows][256] are 16-byte aligned; part_lse is fp32
- * [rows][splits]; head_dim must be 256.
+ * [rows][splits], 4-byte aligned; head_dim must be 256.
  */
 int paged_gqa_merge_partials(const float* part_o, const float* part_lse, int32_t rows,
                              int32_t splits, int32_t head_dim, void* out, void* stream);

@@ -140,7 +140,9 @@ def test_partial_and_merge_validation(lib):
     assert lib.paged_gqa_decode_partial(*args(q=None)) == E.PGQA_ERR_NULL
     assert lib.paged_gqa_decode_partial(*args(po=None)) == E.PGQA_ERR_NULL
     assert lib.paged_gqa_decode_partial(*args(pl=None)) == E.PGQA_ERR_NULL
-    assert lib.paged_gqa_decode_partial(*args(pl=FAKE * 8 + 4)) == E.PGQA_ERR_LAYOUT
+    # part_lse takes 4-byte alignment only (the kernels store and load it as
+    # single floats).
+    assert lib.paged_gqa_decode_partial(*args(pl=FAKE * 8 + 2)) == E.PGQA_ERR_LAYOUT
     assert lib.paged_gqa_decode_partial(*args(d=64)) == E.PGQA_ERR_SHAPE
     m = lib.paged_gqa_merge_partials
     assert m(FAKE, FAKE, 10, 4, 128, FAKE, None) == E.PGQA_ERR_SHAPE
@@ -149,6 +151,7 @@ def test_partial_and_merge_validation(lib):
     assert m(None, FAKE, 10, 4, 256, FAKE, None) == E.PGQA_ERR_NULL
     assert m(FAKE, FAKE, 10, 4, 256, None, None) == E.PGQA_ERR_NULL
     assert m(FAKE + 8, FAKE, 10, 4, 256, FAKE, None) == E.PGQA_ERR_LAYOUT
+    assert m(FAKE, FAKE + 2, 10, 4, 256, FAKE, None) == E.PGQA_ERR_LAYOUT
     assert m(None, None, 0, 4, 256, None, None) == E.PGQA_OK  # nothing to do
 
 

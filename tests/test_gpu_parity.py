@@ -344,6 +344,34 @@ def test_reused_workspace_and_empty_rows(pg):
     assert_parity(outs[0], ref, "reused workspace")
 
 
+@pytest.mark.parametrize("batch,length,splits,S", [
+    (1, 8256, 17, 17), (1, 8448, 33, 33), (3, 2560, 40, 40), (1, 16384, 128, 128),
+    (2, 9000, 0, 71)])
+def test_split_counts_against_oracle(pg, batch, length, splits, S):
+    """Split counts that are not powers of two, with a partial last split
+    (8256 = 16 * 512 + 64 tokens in 17 splits), against the oracle and
+    repeated bit for bit on the same workspace."""
+    import torch
+
+    case = inputs.decode_case(batch=batch, lens=[length] * batch, page_size=128,
+                              kv_dtype=E4M3, seed=300 + splits, scales="uniform")
+    q, pool, table, lens = pg.device_case(case)
+    n, hq, _ = q.shape
+    assert pg.paged_gqa_num_splits(n, 1, case.max_seq_len, splits) == S
+    wsb = pg.paged_gqa_workspace_bytes(n, hq, 1, case.max_seq_len, splits)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    ref = oracle.paged_gqa(**case.oracle_kwargs())
+    got = []
+    for _ in range(2):
+        out = torch.empty_like(q)
+        pg.paged_gqa_decode(q, pool, table, lens, case.max_seq_len, case.sm_scale, out,
+                            workspace=ws, num_splits=splits)
+        torch.cuda.synchronize()
+        got.append(out.cpu().numpy())
+    assert_parity(got[0], ref, f"S={S}")
+    assert np.array_equal(got[0].view(np.uint16), got[1].view(np.uint16))
+
+
 @pytest.mark.parametrize("splits", [2, 5, 0])
 def test_partial_then_merge_equals_decode_bitwise(pg, splits):
     """With every length at (or clamped to) max_seq_len a whole call uses the
