@@ -10,6 +10,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "pgqa.h"
 #include "pgqa_internal.h"
@@ -39,6 +40,36 @@ constexpr int kRowPerWaveMaxLen = 4096;
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
+
+// Split partials of paged_gqa_decode_noalloc.  Each device holds its own copy
+// at its own address; host code uses only the address hipGetSymbolAddress
+// returns for the current device (the array's name on the host is a
+// stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[PGQA_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's scratch, looked up once per device
+// with that device current.
+hipError_t current_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -260,6 +291,28 @@ int paged_gqa_decode(const void* q, const pgqa_kv_pool* kv, const int32_t* page_
                        workspace_bytes, stream,
                        // Each K/V byte is read once per call: non-temporal loads.
                        /*stream_kv=*/true);
+}
+
+int paged_gqa_decode_noalloc(const void* q, const pgqa_kv_pool* kv, const int32_t* page_table,
+                             int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len,
+                             int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, float sm_scale, int32_t num_splits, void* out,
+                             void* stream) {
+  // The size check comes before the scratch lookup, so an oversized call is
+  // rejected without any HIP call when num_splits is explicit.
+  int rc = validate_call(q, kv, page_table, max_pages, seq_lens, max_seq_len, batch, num_q_heads,
+                         num_kv_heads, head_dim, sm_scale, num_splits, out);
+  if (rc != PGQA_OK || batch == 0) return rc;
+  SplitPlan plan;
+  rc = plan_call(batch, num_kv_heads, max_seq_len, num_splits, &plan);
+  if (rc != PGQA_OK) return rc;
+  const size_t need = workspace_need(batch, num_q_heads, num_kv_heads, plan.splits);
+  if (need > PGQA_NOALLOC_SCRATCH_BYTES) return PGQA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && current_scratch(&ws) != hipSuccess) return PGQA_ERR_HIP;
+  return run_attention(q, kv, page_table, max_pages, seq_lens, max_seq_len, batch, num_q_heads,
+                       num_kv_heads, head_dim, sm_scale, num_splits, out, ws,
+                       need > 0 ? PGQA_NOALLOC_SCRATCH_BYTES : 0, stream, /*stream_kv=*/true);
 }
 
 int paged_gqa_prefill_sparse(const void* q, const pgqa_kv_pool* kv, const int32_t* row_tables,

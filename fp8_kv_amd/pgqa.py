@@ -29,10 +29,12 @@ PGQA_KV_FP16 = 0
 PGQA_KV_E4M3 = 1
 HEAD_DIM = 256
 SIZE_MAX = ctypes.c_size_t(-1).value
+NOALLOC_SCRATCH_BYTES = 8 << 20  # PGQA_NOALLOC_SCRATCH_BYTES
 
 # Every symbol include/pgqa.h declares.
 EXPORTS = ("paged_gqa_workspace_bytes", "paged_gqa_num_splits", "paged_gqa_decode",
            "paged_gqa_prefill_sparse", "paged_gqa_decode_partial", "paged_gqa_merge_partials",
+           "paged_gqa_decode_noalloc",
            "e4m3_decode_table", "qsa_topk_select", "qsa_build_page4_table",
            "sampler_topk_topp_workspace_bytes", "sampler_topk_topp_mask", "pgqa_error_string")
 QSA_MAX_BLOCKS = 65536
@@ -91,6 +93,9 @@ def _lib(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_gqa_decode_partial.restype = ctypes.c_int
     lib.paged_gqa_decode_partial.argtypes = [vp, ctypes.POINTER(KVPoolC), vp, i32, vp, i32, i32,
                                              i32, i32, i32, f32, i32, vp, vp, vp]
+    lib.paged_gqa_decode_noalloc.restype = ctypes.c_int
+    lib.paged_gqa_decode_noalloc.argtypes = [vp, ctypes.POINTER(KVPoolC), vp, i32, vp, i32, i32,
+                                             i32, i32, i32, f32, i32, vp, vp]
     lib.paged_gqa_merge_partials.restype = ctypes.c_int
     lib.paged_gqa_merge_partials.argtypes = [vp, vp, i32, i32, i32, vp, vp]
     lib.e4m3_decode_table.restype = ctypes.c_int
@@ -266,6 +271,26 @@ def _call(fn_name, q, kv, table, lens, max_len, hkv, sm_scale, num_splits, out, 
         int(max_len), int(n), int(hq), int(hkv), int(d), float(sm_scale), int(num_splits),
         _ptr(out), _ptr(workspace), int(ws_bytes), _stream_handle(stream))
     _check(rc, fn_name)
+
+
+def paged_gqa_decode_noalloc(q, kv: KVPool, page_table, seq_lens, max_seq_len: int,
+                             sm_scale: float, out, num_kv_heads: int = 1, num_splits: int = 0,
+                             stream=None) -> None:
+    """paged_gqa_decode without a workspace: the split partials live in the
+    library's per-device scratch (at most PGQA_NOALLOC_SCRATCH_BYTES), so the
+    call allocates nothing.  Calls that overlap on one GPU race."""
+    import torch
+
+    _check_inputs(q, kv, page_table, seq_lens, num_kv_heads)
+    _expect(out, "out", torch.float16, tuple(q.shape))
+    _device(q=q, page_table=page_table, lengths=seq_lens, kv_k=kv.k, kv_v=kv.v, out=out)
+    n, hq, d = q.shape
+    c_pool = kv.as_c()
+    rc = _lib().paged_gqa_decode_noalloc(
+        _ptr(q), ctypes.byref(c_pool), _ptr(page_table), int(page_table.shape[1]),
+        _ptr(seq_lens), int(max_seq_len), int(n), int(hq), int(num_kv_heads), int(d),
+        float(sm_scale), int(num_splits), _ptr(out), _stream_handle(stream))
+    _check(rc, "paged_gqa_decode_noalloc")
 
 
 def paged_gqa_decode_partial(q, kv: KVPool, page_table, seq_lens, max_seq_len: int,

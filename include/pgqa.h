@@ -173,6 +173,29 @@ int paged_gqa_prefill_sparse(const void* q, const pgqa_kv_pool* kv, const int32_
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paged_gqa_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, the same result bit for bit.
+ * The split partials go to a scratch array inside the library, one per GPU
+ * (PGQA_NOALLOC_SCRATCH_BYTES bytes, held by every GPU the call runs on until
+ * the process ends).  The call allocates nothing, takes no workspace and
+ * needs none cleared: every scratch byte it reads it has written itself.
+ * Calls that overlap on one GPU (two streams, two threads) share that GPU's
+ * scratch and race; serialise them.  The first call on a device looks up
+ * that device's scratch address (a HIP symbol query, no allocation).
+ * Errors: those of paged_gqa_decode; PGQA_ERR_WORKSPACE when
+ * paged_gqa_workspace_bytes(...) for the call exceeds
+ * PGQA_NOALLOC_SCRATCH_BYTES (nothing is launched); PGQA_ERR_HIP when the
+ * scratch address cannot be obtained or a launch is refused.
+ */
+#define PGQA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int paged_gqa_decode_noalloc(const void* q, const pgqa_kv_pool* kv, const int32_t* page_table,
+                             int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len,
+                             int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, float sm_scale, int32_t num_splits, void* out,
+                             void* stream);
+
+/*
  * First stage of paged_gqa_decode alone: per-split partial results, for
  * callers that merge them themselves (e.g. shards of one sequence computed on
  * different devices).  Same arguments as paged_gqa_decode up to num_splits.

@@ -116,6 +116,29 @@ def test_validation_errors(lib, fn):
     assert c(n=0, q=None, out=None, table=None, lens=None) == E.PGQA_OK
 
 
+def test_noalloc_rejects_before_any_hip_call(lib):
+    """The no-allocation decode validates like paged_gqa_decode and rejects a
+    call whose partials exceed its scratch (explicit splits: no device
+    query, nothing launched)."""
+    text = open(os.path.join(ROOT, "include", "pgqa.h")).read()
+    m = re.search(r"#define PGQA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pgqa.NOALLOC_SCRATCH_BYTES
+
+    def c(q=FAKE, kv=None, n=2, hq=6, hkv=1, d=256, max_len=1024, max_pages=64, splits=4):
+        kv = pool() if kv is None else kv
+        return lib.paged_gqa_decode_noalloc(q, ctypes.byref(kv), FAKE, max_pages, FAKE, max_len,
+                                            n, hq, hkv, d, 0.0625, splits, FAKE * 2, None)
+    assert c(q=None) == pgqa.PGQA_ERR_NULL
+    assert c(d=128) == pgqa.PGQA_ERR_SHAPE
+    assert c(splits=-1) == pgqa.PGQA_ERR_ARG
+    assert c(n=0) == pgqa.PGQA_OK  # nothing to do
+    # 64 sequences x 16 heads x 8 splits of (256 + 1) floats: just over 8 MiB.
+    big = lib.paged_gqa_workspace_bytes(64, 16, 1, 256, 1024, 8)
+    assert big == 64 * 16 * 8 * 257 * 4 > pgqa.NOALLOC_SCRATCH_BYTES
+    assert c(n=64, hq=16, splits=8) == pgqa.PGQA_ERR_WORKSPACE
+    assert lib.paged_gqa_workspace_bytes(64, 16, 1, 256, 1024, 7) <= pgqa.NOALLOC_SCRATCH_BYTES
+
+
 def test_workspace_bytes(lib):
     ws = lib.paged_gqa_workspace_bytes
     assert ws(16, 6, 1, 256, 16384, 32) == 16 * 6 * 32 * 257 * 4
