@@ -84,6 +84,26 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u4_t* __res
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// One wave reads the shader-clock counter (s_memtime) and the constant
+// 100 MHz real-time counter (s_memrealtime) at the start and end of a spin of
+// about `ticks` real-time ticks; out[0] = real-time ticks elapsed, out[1] =
+// shader-clock ticks over the same interval.  The spin ends after at most
+// kMaxProbeIters iterations whatever the counters do.
+constexpr int kMaxProbeIters = 1 << 22;
+__global__ void clock_probe_kernel(uint64_t* out, uint32_t ticks) {
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  uint64_t r1 = r0, t1 = t0;
+  for (int i = 0; i < kMaxProbeIters && r1 - r0 < ticks; ++i) {
+    r1 = __builtin_amdgcn_s_memrealtime();
+    t1 = __builtin_amdgcn_s_memtime();
+  }
+  if (threadIdx.x == 0) {
+    out[0] = r1 - r0;
+    out[1] = t1 - t0;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,6 +136,23 @@ int stream_read(const void* a, size_t a_bytes, const void* b, size_t b_bytes, in
                                 na, pb, per_block, n, ps)
           : pgqa_launch::launch(stream_read_kernel<false>, dim3(blocks), dim3(kThreads), 0, st,
                                 pa, na, pb, per_block, n, ps);
+  return e == hipSuccess ? 0 : -4;
+}
+
+// Shader clock over a short spin (benchmark bookkeeping: the clock the
+// device ran at right after a timed batch).  out: device memory of two
+// uint64 (8-byte aligned): real-time ticks (100 MHz) and shader-clock ticks
+// over the same interval, so MHz = 100 * out[1] / out[0].  ticks: spin
+// length in real-time ticks, 1..100000 (10 ns each).  Returns 0, -1 (out
+// NULL), -2 (ticks out of range), -3 (out not 8-byte aligned) or -4 (launch
+// failed).  Asynchronous.
+int clock_probe(void* out, int32_t ticks, void* stream) {
+  if (!out) return -1;
+  if (ticks < 1 || ticks > 100000) return -2;
+  if (reinterpret_cast<uintptr_t>(out) & 7) return -3;
+  const hipError_t e =
+      pgqa_launch::launch(clock_probe_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                          static_cast<uint64_t*>(out), static_cast<uint32_t>(ticks));
   return e == hipSuccess ? 0 : -4;
 }
 

@@ -25,6 +25,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
         lib.stream_read.restype = ctypes.c_int
         lib.stream_read.argtypes = [vp, sz, vp, sz, ctypes.c_int32, ctypes.c_int32, vp, vp]
+        lib.clock_probe.restype = ctypes.c_int
+        lib.clock_probe.argtypes = [vp, ctypes.c_int32, vp]
         _LIB = lib
     return _LIB
 
@@ -44,3 +46,19 @@ def stream_read(a, b, sink, blocks: int, nontemporal: bool = True, stream=None) 
                             blocks, int(nontemporal), sink.data_ptr(), stream.cuda_stream)
     if rc != 0:
         raise RuntimeError(f"stream_read: {_ERRORS.get(rc, rc)} (code {rc})")
+
+
+def clock_mhz(buf, ticks: int = 2000, stream=None) -> float:
+    """Shader clock in MHz over a spin of `ticks` 10-ns real-time ticks, run
+    on `stream` (synchronises it).  buf: int64 device tensor of at least 2
+    elements (scratch for the two counters)."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    rc = load().clock_probe(buf.data_ptr(), int(ticks), stream.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"clock_probe: {_ERRORS.get(rc, rc)} (code {rc})")
+    stream.synchronize()
+    real, shader = buf[:2].tolist()
+    return 100.0 * shader / max(real, 1)

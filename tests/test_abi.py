@@ -329,6 +329,11 @@ def test_stream_read_library_validation():
     assert f(FAKE + 8, 64, None, 0, 4, 1, FAKE, None) == -3      # alignment
     assert f(FAKE, 64, FAKE + 4, 16, 4, 1, FAKE, None) == -3
     assert f(FAKE, 64, None, 0, 4, 1, FAKE + 8, None) == -3
+    p = lib.clock_probe
+    assert p(None, 100, None) == -1
+    assert p(FAKE, 0, None) == -2
+    assert p(FAKE, 100001, None) == -2
+    assert p(FAKE + 4, 100, None) == -3
 
 
 def test_explicit_split_counts(lib):

@@ -41,7 +41,7 @@ def test_committed_traffic_is_plausible():
     algorithmic KV bytes (no byte fetched twice)."""
     import pytest
 
-    t = bench.measured_traffic(bench.kernel_source_hash())
+    t = bench.measured_traffic(bench.kernel_source_hash(), "decode_b16_16k_e4m3_p128")
     if t is None:
         pytest.skip("counters not yet retaken on the current attention sources")
     assert 134_217_728 < t < 1.05 * 134_217_728

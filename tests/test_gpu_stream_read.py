@@ -50,3 +50,16 @@ def test_checksums(dev, a_words, b_words, blocks, nt):
     torch.cuda.synchronize()
     got = sink.cpu().numpy().view(np.uint32)
     assert np.array_equal(got, expected(np.concatenate([a, b]), blocks))
+
+
+def test_clock_probe_plausible(dev):
+    """The shader-clock probe the benchmark reads after each timed batch
+    returns a spin of at least the asked length and a clock between 0.3 and
+    4 GHz."""
+    from fp8_kv_amd import stream_read
+
+    buf = torch.zeros(2, dtype=torch.int64, device=dev)
+    mhz = stream_read.clock_mhz(buf, ticks=1000)
+    real = int(buf[0])
+    assert real >= 1000
+    assert 300.0 < mhz < 4000.0
