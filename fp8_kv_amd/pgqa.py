@@ -77,6 +77,11 @@ def _lib(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise FileNotFoundError(
             f"{path} is not built; run `python -m fp8_kv_amd.build` (there is no fallback)")
+    # torch ships its own HIP runtime: load it first so that this library
+    # binds to that same runtime (and sees the tensors torch allocates)
+    # instead of starting a second one from the system ROCm.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(path)
     vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                              ctypes.c_size_t)

@@ -21,6 +21,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if _LIB is None:
         if not os.path.exists(path):
             raise FileNotFoundError(f"{path} is not built; run `python -m fp8_kv_amd.build`")
+        # torch ships its own HIP runtime: load it first so that this library
+        # binds to that same runtime (and sees the tensors torch allocates)
+        # instead of starting a second one from the system ROCm.
+        import torch  # noqa: F401
+
         lib = ctypes.CDLL(path)
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
         lib.stream_read.restype = ctypes.c_int
