@@ -4,6 +4,7 @@
 // any HIP call: an argument error launches nothing and writes nothing.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cstdint>
 
@@ -13,6 +14,26 @@
 namespace {
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+// Compute units of the current device (cached per device), or -1 if HIP
+// cannot say.
+int current_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices) {
+    const int cached = g_cus[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return -1;
+  if (dev < kMaxDevices) g_cus[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 }  // namespace
 
@@ -40,6 +61,8 @@ int qsa_topk_select(const float* scores, int64_t row_stride, const int32_t* n_va
   p.k = k;
   p.out_idx = out_idx;
   p.out_count = out_count;
+  p.grid = current_cus();
+  if (p.grid <= 0) return PGQA_ERR_HIP;
   const bool vec = aligned(scores, 16) && row_stride % 4 == 0 && n_blocks % 4 == 0;
   if (qsa::launch_topk(p, vec, static_cast<hipStream_t>(stream)) != hipSuccess)
     return PGQA_ERR_HIP;

@@ -21,6 +21,7 @@ struct TopkParams {
   int32_t k;
   int32_t* out_idx;        // [rows][k]
   int32_t* out_count;      // [rows] or nullptr
+  int32_t grid;            // workgroups (>= 1): each takes every grid-th row
 };
 
 // vec: scores 16-byte aligned, row_stride and n_blocks multiples of 4.

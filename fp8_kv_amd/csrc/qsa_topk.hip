@@ -271,35 +271,23 @@ __device__ __forceinline__ Pivot pivot_regions(TopkShared& sh, uint32_t k, uint3
   return pv;
 }
 
-template <int ITEMS, bool VEC>
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
-  __shared__ TopkShared sh;
-  const int row = blockIdx.x;
+// Row r's eligible length n_valid[r] clamped to [0, n_blocks].
+__device__ __forceinline__ int32_t row_valid(const TopkParams& p, int row) {
+  const int32_t nv = p.n_valid ? p.n_valid[row] : p.n_blocks;
+  return nv < 0 ? 0 : (nv > p.n_blocks ? p.n_blocks : nv);
+}
+
+// Loads register slots I0 .. I1 - 1 of row `row` into x: element (i, c) of
+// this thread is j = 4096 i + 4 tid + c, valid when j < nv.  Invalid elements
+// hold -inf.
+template <int ITEMS, bool VEC, int I0, int I1>
+__device__ __forceinline__ void load_row(uint32_t (&x)[ITEMS][4], const TopkParams& p, int row,
+                                         int32_t nv) {
   const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int32_t k = p.k;
-  int32_t nv = p.n_valid ? p.n_valid[row] : p.n_blocks;
-  nv = nv < 0 ? 0 : (nv > p.n_blocks ? p.n_blocks : nv);
-  int32_t* out = p.out_idx + static_cast<int64_t>(row) * k;
-
-  if (nv <= k) {  // every eligible block is kept
-    for (int j = tid; j < k; j += kThreads) out[j] = j < nv ? j : -1;
-    if (tid == 0 && p.out_count) p.out_count[row] = nv;
-    return;
-  }
-  if (k == 0) {
-    if (tid == 0 && p.out_count) p.out_count[row] = 0;
-    return;
-  }
-
-  // ---- load: element (i, c) of this thread is j = 4096 i + 4 tid + c, valid
-  // when 4096 i + c < lim.  Invalid elements hold -inf.
   const float* src = p.scores + static_cast<int64_t>(row) * p.row_stride;
   const int32_t lim = nv - 4 * tid;
-  uint32_t x[ITEMS][4];
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
+  for (int i = I0; i < I1; ++i) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) x[i][c] = kNegInfBits;
     if (i * kSlotElems < nv) {
@@ -335,6 +323,48 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
       }
     }
   }
+}
+
+// Workgroup w takes rows w, w + G, w + 2G, ... (G = gridDim.x).  A row's
+// scores are needed in registers only up to the candidate pass: the loads of
+// the next row's first kPre slots are issued right after it, so they are in
+// flight while this row's pivot, bitmaps and output run on LDS (all slots
+// in flight there would exceed the 128 registers a 16-wave workgroup has);
+// its other slots are loaded when that row starts.
+template <int ITEMS, bool VEC>
+__global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
+  constexpr int kPre = ITEMS > 1 ? ITEMS / 2 : ITEMS;
+  __shared__ TopkShared sh;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t k = p.k;
+  int row = blockIdx.x;
+  int32_t nv = row_valid(p, row);
+  uint32_t x[ITEMS][4];
+  if (nv > k && k > 0) load_row<ITEMS, VEC, 0, kPre>(x, p, row, nv);
+  for (; row < p.rows; row += gridDim.x) {
+  // An opaque copy of the thread index per row: index arithmetic derived
+  // from it is recomputed in each row instead of being hoisted out of the
+  // loop and held in registers (spilled) across rows.
+  int tid_row = static_cast<int>(threadIdx.x);
+  asm volatile("" : "+v"(tid_row));
+  const int tid = tid_row;
+  const int next = row + static_cast<int>(gridDim.x);
+  const int32_t nv_next = next < p.rows ? row_valid(p, next) : 0;
+  const bool load_next = next < p.rows && nv_next > k && k > 0;
+  int32_t* out = p.out_idx + static_cast<int64_t>(row) * k;
+  const float* src = p.scores + static_cast<int64_t>(row) * p.row_stride;
+  const int32_t lim = nv - 4 * tid;
+
+  if (nv <= k || k == 0) {  // every eligible block is kept (none when k = 0)
+    for (int j = tid; j < k; j += kThreads) out[j] = j < nv ? j : -1;
+    if (tid == 0 && p.out_count) p.out_count[row] = nv <= k ? nv : 0;
+    if (load_next) load_row<ITEMS, VEC, 0, kPre>(x, p, next, nv_next);
+    nv = nv_next;
+    continue;
+  }
+  load_row<ITEMS, VEC, kPre, ITEMS>(x, p, row, nv);
 
   // Shared state for the phases below.
   if (tid < 256) {
@@ -421,6 +451,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   const uint32_t used = cnt < static_cast<uint32_t>(kRegion) ? cnt : kRegion;
   const uint2* region = sh.cand + kRegion * wave;
   __syncthreads();
+  // The scores of this row are no longer needed in registers.
+  if (load_next) load_row<ITEMS, VEC, 0, kPre>(x, p, next, nv_next);
 
   // ---- 3. the pivot over the candidates with key >= T (all waves, each
   // over its own region).  Candidates with key in [T, top] share the leading
@@ -510,15 +542,19 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
     w1 &= w1 - 1u;
   }
   if (tid == 0 && p.out_count) p.out_count[row] = k;
+  nv = nv_next;
+  // Every thread has read this row's bitmaps before the next row clears them.
+  __syncthreads();
+  }
 }
 
 template <int ITEMS>
 hipError_t launch_items(const TopkParams& p, bool vec, hipStream_t stream) {
-  if (vec)
-    return pgqa_launch::launch(topk_kernel<ITEMS, true>, dim3(p.rows), dim3(kThreads), 0, stream,
-                               p);
-  return pgqa_launch::launch(topk_kernel<ITEMS, false>, dim3(p.rows), dim3(kThreads), 0, stream,
-                             p);
+  // One workgroup per compute unit (16 waves and 96 VGPRs each: one fits),
+  // each walking its rows.
+  const dim3 grid(static_cast<unsigned>(p.rows < p.grid ? p.rows : p.grid));
+  if (vec) return pgqa_launch::launch(topk_kernel<ITEMS, true>, grid, dim3(kThreads), 0, stream, p);
+  return pgqa_launch::launch(topk_kernel<ITEMS, false>, grid, dim3(kThreads), 0, stream, p);
 }
 
 }  // namespace

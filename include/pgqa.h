@@ -263,7 +263,7 @@ int e4m3_decode_table(float* out256, void* stream);
  * Errors: PGQA_ERR_NULL (scores, or out_idx with k > 0, missing while
  * rows > 0), PGQA_ERR_SHAPE (negative rows/k, n_blocks or k out of range),
  * PGQA_ERR_LAYOUT (row_stride < n_blocks or misaligned pointers),
- * PGQA_ERR_HIP (launch refused).
+ * PGQA_ERR_HIP (the compute-unit count query or the launch refused).
  */
 #define PGQA_QSA_MAX_BLOCKS 65536 /* 262,144 tokens in 4-token blocks */
 int qsa_topk_select(const float* scores, int64_t row_stride, const int32_t* n_valid,
