@@ -271,6 +271,103 @@ __device__ __forceinline__ Pivot pivot_regions(TopkShared& sh, uint32_t k, uint3
   return pv;
 }
 
+// Phases 3-5 of one row, once the candidates are in the wave regions:
+// pivot, bitmaps, ordered output (and the exact fallback over the row in
+// memory when the candidate pass cannot decide).
+__device__ __forceinline__ void finish_row(TopkShared& sh, const TopkParams& p, int row,
+                                           int32_t k, int32_t nv, int tid, int lane, uint32_t T,
+                                           uint32_t top, bool float_cand, const uint2* region,
+                                           uint32_t used, const float* src, int32_t* out) {
+  // ---- 3. the pivot over the candidates with key >= T (all waves, each
+  // over its own region).  Candidates with key in [T, top] share the leading
+  // bytes of T and top.
+  const uint32_t kk = static_cast<uint32_t>(k);
+  int first = 0;
+  if (float_cand) {
+    const uint32_t diff = T ^ top;
+    first = diff == 0 ? 3 : (__clz(diff) >> 3);
+  }
+  Pivot pv = pivot_regions(sh, kk, T, first, region, used);
+  const bool fast_pivot = pv.ok;
+  if (!fast_pivot) {
+    // Exact passes over the whole row, re-read from cache, once every wave
+    // has left the candidate passes.
+    __syncthreads();
+    if (tid < 256) {
+      sh.hist[0][tid] = 0;
+      sh.hist[1][tid] = 0;
+    }
+    __syncthreads();
+    pv = pivot_block(sh, kk, [&](auto f) {
+      for (int32_t b = 0; b < nv; b += kThreads) {
+        const int32_t j = b + tid;
+        f(j < nv, j < nv ? key_of_bits(__float_as_uint(src[j])) : 0u);
+      }
+    });
+  }
+  const uint32_t P = pv.key;
+  const bool split_ties = pv.eq != pv.need;  // only some of the pivot's ties are kept
+
+  // ---- 4. bitmaps of kept and (when only some are kept) tied blocks.
+  auto mark = [&](uint32_t key, uint32_t j) {
+    const uint32_t bit = 1u << (j & 31);
+    if (split_ties ? key > P : key >= P) atomicOr(&sh.keep[j >> 5], bit);
+    if (split_ties && key == P) atomicOr(&sh.tied[j >> 5], bit);
+  };
+  if (fast_pivot) {
+    // Every block with key >= P >= T is a candidate.
+    for (uint32_t b = 0; b < used; b += 64) {
+      const uint32_t e = b + lane;
+      if (e < used) {
+        const uint2 cj = region[e];
+        mark(key_of_bits(cj.x), cj.y);
+      }
+    }
+  } else {
+    for (int32_t b = 0; b < nv; b += kThreads) {
+      const int32_t j = b + tid;
+      if (j < nv) mark(key_of_bits(__float_as_uint(src[j])), static_cast<uint32_t>(j));
+    }
+  }
+  __syncthreads();
+  uint32_t w0 = sh.keep[2 * tid];
+  uint32_t w1 = sh.keep[2 * tid + 1];
+  if (split_ties) {
+    // Keep the first `need` tied blocks in index order.
+    uint32_t q0 = sh.tied[2 * tid];
+    uint32_t q1 = sh.tied[2 * tid + 1];
+    const uint32_t qc = __popc(q0) + __popc(q1);
+    const uint32_t before = block_excl_scan(qc, sh.wsum[0]);
+    uint32_t take = before < pv.need ? pv.need - before : 0u;
+    while (take > 0 && q0) {
+      w0 |= q0 & (0u - q0);
+      q0 &= q0 - 1u;
+      --take;
+    }
+    while (take > 0 && q1) {
+      w1 |= q1 & (0u - q1);
+      q1 &= q1 - 1u;
+      --take;
+    }
+  }
+
+  // ---- 5. ordered output of blocks 64 tid .. 64 tid + 63.
+  uint32_t pos = block_excl_scan(__popc(w0) + __popc(w1), sh.wsum[1]);
+  while (w0) {
+    const int b = __ffs(w0) - 1;
+    if (pos < kk) out[pos] = 64 * tid + b;
+    ++pos;
+    w0 &= w0 - 1u;
+  }
+  while (w1) {
+    const int b = __ffs(w1) - 1;
+    if (pos < kk) out[pos] = 64 * tid + 32 + b;
+    ++pos;
+    w1 &= w1 - 1u;
+  }
+  if (tid == 0 && p.out_count) p.out_count[row] = k;
+}
+
 // Row r's eligible length n_valid[r] clamped to [0, n_blocks].
 __device__ __forceinline__ int32_t row_valid(const TopkParams& p, int row) {
   const int32_t nv = p.n_valid ? p.n_valid[row] : p.n_blocks;
@@ -454,94 +551,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   // The scores of this row are no longer needed in registers.
   if (load_next) load_row<ITEMS, VEC, 0, kPre>(x, p, next, nv_next);
 
-  // ---- 3. the pivot over the candidates with key >= T (all waves, each
-  // over its own region).  Candidates with key in [T, top] share the leading
-  // bytes of T and top.
-  const uint32_t kk = static_cast<uint32_t>(k);
-  int first = 0;
-  if (float_cand) {
-    const uint32_t diff = T ^ top;
-    first = diff == 0 ? 3 : (__clz(diff) >> 3);
-  }
-  Pivot pv = pivot_regions(sh, kk, T, first, region, used);
-  const bool fast_pivot = pv.ok;
-  if (!fast_pivot) {
-    // Exact passes over the whole row, re-read from cache, once every wave
-    // has left the candidate passes.
-    __syncthreads();
-    if (tid < 256) {
-      sh.hist[0][tid] = 0;
-      sh.hist[1][tid] = 0;
-    }
-    __syncthreads();
-    pv = pivot_block(sh, kk, [&](auto f) {
-      for (int32_t b = 0; b < nv; b += kThreads) {
-        const int32_t j = b + tid;
-        f(j < nv, j < nv ? key_of_bits(__float_as_uint(src[j])) : 0u);
-      }
-    });
-  }
-  const uint32_t P = pv.key;
-  const bool split_ties = pv.eq != pv.need;  // only some of the pivot's ties are kept
-
-  // ---- 4. bitmaps of kept and (when only some are kept) tied blocks.
-  auto mark = [&](uint32_t key, uint32_t j) {
-    const uint32_t bit = 1u << (j & 31);
-    if (split_ties ? key > P : key >= P) atomicOr(&sh.keep[j >> 5], bit);
-    if (split_ties && key == P) atomicOr(&sh.tied[j >> 5], bit);
-  };
-  if (fast_pivot) {
-    // Every block with key >= P >= T is a candidate.
-    for (uint32_t b = 0; b < used; b += 64) {
-      const uint32_t e = b + lane;
-      if (e < used) {
-        const uint2 cj = region[e];
-        mark(key_of_bits(cj.x), cj.y);
-      }
-    }
-  } else {
-    for (int32_t b = 0; b < nv; b += kThreads) {
-      const int32_t j = b + tid;
-      if (j < nv) mark(key_of_bits(__float_as_uint(src[j])), static_cast<uint32_t>(j));
-    }
-  }
-  __syncthreads();
-  uint32_t w0 = sh.keep[2 * tid];
-  uint32_t w1 = sh.keep[2 * tid + 1];
-  if (split_ties) {
-    // Keep the first `need` tied blocks in index order.
-    uint32_t q0 = sh.tied[2 * tid];
-    uint32_t q1 = sh.tied[2 * tid + 1];
-    const uint32_t qc = __popc(q0) + __popc(q1);
-    const uint32_t before = block_excl_scan(qc, sh.wsum[0]);
-    uint32_t take = before < pv.need ? pv.need - before : 0u;
-    while (take > 0 && q0) {
-      w0 |= q0 & (0u - q0);
-      q0 &= q0 - 1u;
-      --take;
-    }
-    while (take > 0 && q1) {
-      w1 |= q1 & (0u - q1);
-      q1 &= q1 - 1u;
-      --take;
-    }
-  }
-
-  // ---- 5. ordered output of blocks 64 tid .. 64 tid + 63.
-  uint32_t pos = block_excl_scan(__popc(w0) + __popc(w1), sh.wsum[1]);
-  while (w0) {
-    const int b = __ffs(w0) - 1;
-    if (pos < kk) out[pos] = 64 * tid + b;
-    ++pos;
-    w0 &= w0 - 1u;
-  }
-  while (w1) {
-    const int b = __ffs(w1) - 1;
-    if (pos < kk) out[pos] = 64 * tid + 32 + b;
-    ++pos;
-    w1 &= w1 - 1u;
-  }
-  if (tid == 0 && p.out_count) p.out_count[row] = k;
+  finish_row(sh, p, row, k, nv, tid, lane, T, top, float_cand, region, used, src, out);
   nv = nv_next;
   // Every thread has read this row's bitmaps before the next row clears them.
   __syncthreads();
