@@ -11,10 +11,13 @@
 // u ^ (sign ? 0xFFFFFFFF : 0x80000000), which orders scores like IEEE 754
 // totalOrder (-NaN < -inf < ... < -0 < +0 < ... < +inf < +NaN).
 //
-// One workgroup of 1024 threads (16 waves) owns one row.  Thread t holds
-// elements j = 4096 i + 4 t + c (register slot i, component c) as raw fp32
-// bits in VGPRs, so a row of up to 65,536 blocks is read from HBM once, with
-// 16-byte coalesced loads.  Elements past the row's length hold -inf.
+// One workgroup of 1024 threads (16 waves) works on one row at a time; with
+// one workgroup per compute unit, workgroup w takes rows w, w + G, ... (G
+// workgroups).  Thread t holds elements j = 4096 i + 4 t + c (register slot
+// i, component c) as raw fp32 bits in VGPRs, so a row of up to 65,536 blocks
+// is read from HBM once, with 16-byte coalesced loads.  Elements past the
+// row's length hold -inf.  The first half of the next row is loaded while
+// the current row is in phases 3-5, which need only LDS.
 //   1. Threshold T (rows longer than 4096 blocks, k <= 1024): each lane's
 //      maximum in key order (from max/min of the signed raw bits), then each
 //      wave's ceil(k/16)-th largest lane maximum by a 32-step ballot
@@ -560,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
 
 template <int ITEMS>
 hipError_t launch_items(const TopkParams& p, bool vec, hipStream_t stream) {
-  // One workgroup per compute unit (16 waves and 96 VGPRs each: one fits),
+  // One workgroup per compute unit (16 waves of up to 128 VGPRs: one fits),
   // each walking its rows.
   const dim3 grid(static_cast<unsigned>(p.rows < p.grid ? p.rows : p.grid));
   if (vec) return pgqa_launch::launch(topk_kernel<ITEMS, true>, grid, dim3(kThreads), 0, stream, p);
