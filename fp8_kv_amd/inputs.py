@@ -258,6 +258,19 @@ WORKLOADS = {
                                      scales="uniform"),
     "decode_ragged_b16_16k_p256": dict(kind="decode", batch=16, lens=("uniform", 1, 16384),
                                         page_size=256, max_seq_len=16384, seed=0),
+    # The other three ragged variants: {FP8, FP16} x {contiguous, interleaved}.
+    "decode_ragged_b16_16k_p256_interleaved": dict(kind="decode", batch=16,
+                                                    lens=("uniform", 1, 16384), page_size=256,
+                                                    max_seq_len=16384, seed=0,
+                                                    layout="interleaved"),
+    "decode_ragged_b16_16k_p256_fp16": dict(kind="decode", batch=16, lens=("uniform", 1, 16384),
+                                             page_size=256, max_seq_len=16384, seed=0,
+                                             kv_dtype=KV_FP16),
+    "decode_ragged_b16_16k_p256_fp16_interleaved": dict(kind="decode", batch=16,
+                                                         lens=("uniform", 1, 16384),
+                                                         page_size=256, max_seq_len=16384,
+                                                         seed=0, kv_dtype=KV_FP16,
+                                                         layout="interleaved"),
     "prefill_sparse_4096x2051_p4": dict(kind="prefill", rows=4096, selected_blocks=512,
                                          tail=3, pool_blocks=65536, layout="interleaved",
                                          seed=0),
