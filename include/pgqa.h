@@ -27,10 +27,11 @@
  *     PGQA_OK means the launch was accepted, and device faults surface at the
  *     caller's next synchronisation, as usual in HIP.
  *   - On an argument error code nothing is launched and no output is written.
- *     PGQA_ERR_HIP means the HIP runtime refused a launch (the status of that
- *     launch itself, not an error left over from earlier HIP calls); a call
- *     that launches two kernels never launches the second after the first
- *     was refused.
+ *     PGQA_ERR_HIP means the HIP runtime refused a query or a launch (the
+ *     status of that call itself, not an error left over from earlier HIP
+ *     calls).  A call that launches two kernels never launches the second
+ *     after the first was refused; if the second is refused, the first has
+ *     run into the workspace only and the output is not written.
  *   - Thread-safe and stateless apart from a per-device cache of the compute
  *     unit count.  Calls may be captured into HIP graphs (no allocation, no
  *     synchronisation, no memset inside).
