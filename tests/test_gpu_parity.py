@@ -355,6 +355,60 @@ def test_prefill_equals_decode_bitwise(pg):
         assert np.array_equal(a, b)
 
 
+def test_one_workspace_across_shapes(pg):
+    """One workspace, never cleared, serves calls of different shapes in
+    turn: equal lengths (bit for bit equal to decode_partial +
+    merge_partials), ragged batches re-dealt by length (including one
+    sequence with 128 chunks, so its merge takes four 32-chunk rounds, and
+    empty sequences), a batch of empty sequences only, 71 splits (a four-wave
+    merge) and FP16.  Every call matches the oracle and a repeat matches bit
+    for bit."""
+    import torch
+
+    cases = [
+        (dict(batch=16, lens=[4096] * 16, page_size=128, kv_dtype=E4M3, seed=401), 16),
+        (dict(batch=3, lens=[4000, 1, 2500], page_size=128, kv_dtype=E4M3, seed=402), 0),
+        (dict(batch=16, lens=[16384] + [64] * 15, page_size=128, kv_dtype=E4M3, seed=403), 16),
+        (dict(batch=5, lens=[3000, 0, 1, 2049, 64], page_size=64, kv_dtype=E4M3, seed=404), 6),
+        (dict(batch=3, lens=[0, 0, 0], page_size=64, kv_dtype=E4M3, seed=405,
+              max_seq_len=2048), 4),
+        (dict(batch=2, lens=[9000, 9000], page_size=128, kv_dtype=E4M3, seed=406), 71),
+        (dict(batch=2, lens=[3000, 3000], page_size=16, kv_dtype=FP16, seed=407), 12),
+    ]
+    built = [(inputs.decode_case(scales="uniform", **kw), kw, splits) for kw, splits in cases]
+    wsb = max(pg.paged_gqa_workspace_bytes(c.lens.shape[0], 6, 1, c.max_seq_len, s)
+              for c, _, s in built)
+    ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device="cuda")  # garbage, not zero
+    first = []
+    for rep in range(2):
+        for i, (case, kw, splits) in enumerate(built):
+            q, pool, table, lens = pg.device_case(case)
+            out = torch.full_like(q, float("nan"))
+            print(f"shapes: rep {rep} case {i} lens {kw['lens'][:4]} splits {splits}", flush=True)
+            pg.paged_gqa_decode(q, pool, table, lens, case.max_seq_len, case.sm_scale, out,
+                                workspace=ws, num_splits=splits)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            if rep == 0:
+                first.append(got)
+                ref = oracle.paged_gqa(**case.oracle_kwargs())
+                assert_parity(got, ref, f"case {i}")
+                if len(set(case.lens.tolist())) == 1 and case.lens[0] > 0:
+                    n, hq, _ = q.shape
+                    S = pg.paged_gqa_num_splits(n, 1, case.max_seq_len, splits)
+                    po = torch.empty((n, hq, S, 256), dtype=torch.float32, device="cuda")
+                    pl = torch.empty((n, hq, S), dtype=torch.float32, device="cuda")
+                    pg.paged_gqa_decode_partial(q, pool, table, lens, case.max_seq_len,
+                                                case.sm_scale, po, pl, num_splits=splits)
+                    merged = torch.empty_like(q)
+                    pg.paged_gqa_merge_partials(po, pl, merged)
+                    torch.cuda.synchronize()
+                    assert np.array_equal(merged.cpu().numpy().view(np.uint16),
+                                          got.view(np.uint16)), f"case {i} two-stage"
+            else:
+                assert np.array_equal(got.view(np.uint16), first[i].view(np.uint16)), f"case {i}"
+
+
 def test_reused_workspace_and_empty_rows(pg):
     import torch
 
