@@ -20,9 +20,10 @@
 // hash set of the general path, which its waves use one at a time.
 //   1. Collection of the full blocks and the causal positions, two ways:
 //      - Expanded layout (no atomics): the row read as chunks of four entries
-//        from its start; a chunk 4b, 4b+1, 4b+2, 4b+3 with b < c is that
-//        full block (compacted by ballot), a chunk of padding,
-//        stale or causal-block positions only adds to the causal mask.  A row
+//        from its start (one 16-byte load each); a chunk 4b, 4b+1, 4b+2,
+//        4b+3 with b < c is that full block (compacted by ballot), a chunk
+//        of padding, stale or causal-block positions only adds to the
+//        causal mask.  A row
 //        with any other chunk takes the general path; so does one whose
 //        sorted ids hold two equal neighbours (a block listed twice, or two
 //        blocks on one physical page: the general path settles which).
@@ -290,10 +291,18 @@ __device__ __forceinline__ Collected collect_hash(const Page4Params& p, const in
 // only adds to the causal mask.  Any other chunk
 // makes the row take the general path (returns false, wave-uniform).  A
 // block listed twice is caught after the sort (adjacent equal ids).
+// WIDE (rows of at least 4 entries): one 16-byte load per chunk (rows are
+// 4-byte aligned, which these loads need).  The 4-entry window a lane reads
+// starts at its chunk, or at the row's last four entries for the partial
+// last chunk and for chunks past the row, so every load stays inside the
+// row; entries past the row are -1.  All of a pass's loads are issued before
+// any window is inspected.
+template <bool WIDE>
 __device__ __forceinline__ bool collect_fast(const Page4Params& p, const int32_t* trow, int32_t L,
                                              int32_t c, int32_t* ids, Collected& out) {
   const int lane = threadIdx.x & 63;
-  const int32_t n_chunks = (p.n_tokens + 3) >> 2;
+  const int32_t nt = p.n_tokens;
+  const int32_t n_chunks = (nt + 3) >> 2;
   int32_t n_full = 0;
   uint32_t tmask = 0;
   bool ok = true;
@@ -302,15 +311,40 @@ __device__ __forceinline__ bool collect_fast(const Page4Params& p, const int32_t
     int32_t t[kChunks][4];
 #pragma unroll
     for (int u = 0; u < kChunks; ++u) {
+      if constexpr (WIDE) {
+        const int32_t first = 4 * (c0 + 64 * u + lane);
+        int4 w;
+        __builtin_memcpy(&w, trow + min(first, nt - 4), sizeof(w));
+        t[u][0] = w.x;
+        t[u][1] = w.y;
+        t[u][2] = w.z;
+        t[u][3] = w.w;
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int32_t i = 4 * (c0 + 64 * u + lane) + e;
-        t[u][e] = i < p.n_tokens ? trow[i] : -1;
+        for (int e = 0; e < 4; ++e) {
+          const int32_t i = 4 * (c0 + 64 * u + lane) + e;
+          t[u][e] = i < nt ? trow[i] : -1;
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < kChunks; ++u) {
       if (c0 + 64 * u >= n_chunks) break;  // wave-uniform
+      if constexpr (WIDE) {
+        if (4 * (c0 + 64 * u + 64) > nt) {  // wave-uniform: the slot reaches past the row
+          // Realign the last chunk's window (shift sh = 1..3) and blank
+          // the entries past the row.
+          const int32_t first = 4 * (c0 + 64 * u + lane);
+          const int32_t sh = first - min(first, nt - 4);
+          const int32_t win[4] = {t[u][0], t[u][1], t[u][2], t[u][3]};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int32_t j = sh + e;
+            const int32_t v = j == 0 ? win[0] : j == 1 ? win[1] : j == 2 ? win[2] : win[3];
+            t[u][e] = first + e < nt ? v : -1;
+          }
+        }
+      }
       // A full block in expanded form: 4b, 4b+1, 4b+2, 4b+3 with b < c.
       const int32_t t0 = t[u][0];
       const uint32_t b0 = static_cast<uint32_t>(t0) >> 2;
@@ -376,7 +410,8 @@ __device__ __forceinline__ RowState attempt(const Page4Params& p, int row, int32
   Collected col;
   if (general)
     col = collect_hash(p, trow, L, c, slots, hmask, hash_log2, ids);
-  else if (!collect_fast(p, trow, L, c, ids, col))
+  else if (!(p.n_tokens >= 4 ? collect_fast<true>(p, trow, L, c, ids, col)
+                              : collect_fast<false>(p, trow, L, c, ids, col)))
     return RowState{0, 0, 0, true};
   const int32_t n_full = col.n_full;
   const uint32_t tmask = wave_or(col.tmask);
