@@ -165,6 +165,32 @@ def test_sequences_and_overflow(dev):
     assert np.all(st & oracle.PAGE4_OVERFLOW)
 
 
+@pytest.mark.parametrize("n_tokens", [1, 2, 3, 4, 5, 6, 7])
+def test_short_rows(dev, n_tokens):
+    """Selections of 1 .. 7 entries: rows shorter than one 16-byte window
+    (read entry by entry) and rows whose last chunk is partial (its window
+    realigned inside the row).  Causal-only rows, a full block with and
+    without causal positions, padding, a stale position and a broken block
+    (general path), each against the oracle bit for bit."""
+    L = 42                                  # causal block c = 10: positions 40, 41
+    rows = [
+        [40, 41],                           # causal only
+        [41, 40],                           # causal, out of order
+        [8, 9, 10, 11, 40, 41],             # full block 2, then causal
+        [8, 9, 10, 11, -1, -1, -1],         # full block, padding
+        [40, 99, 41],                       # a stale position past L
+        [8, 9, 11, 10],                     # block 2 out of order (general path)
+        [-1, -1, -1, -1, 40],               # padding, then causal
+    ]
+    tokens = np.full((len(rows), n_tokens), -1, dtype=np.int32)
+    for r, tok in enumerate(rows):
+        tok = tok[:n_tokens]
+        tokens[r, :len(tok)] = tok
+    btab = np.random.default_rng(n_tokens).permutation(16).astype(np.int32)[None]
+    check(tokens, [L] * len(rows), btab, dev, num_pages=16, page_size=16, vpages_per_page=4,
+          out_stride=4)
+
+
 def test_empty_selection_and_rows(dev):
     tokens = np.zeros((3, 0), np.int32)
     bt = np.arange(4, dtype=np.int32)[None]
