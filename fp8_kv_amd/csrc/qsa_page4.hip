@@ -444,14 +444,15 @@ __device__ __forceinline__ RowState attempt(const Page4Params& p, int row, int32
         b[u] = j < n_pages ? ids[j] : 0;
         lp[u] = pow2 ? (b[u] >> qshift) : b[u] / quarter;
       }
+      // Every entry is loaded (an index past the table reads its last entry)
+      // and judged only once all are issued, so the loads are in flight
+      // together rather than one after another.
+#pragma unroll
+      for (int u = 0; u < kLook; ++u) pg[u] = btab[min(lp[u], p.max_pages - 1)];
 #pragma unroll
       for (int u = 0; u < kLook; ++u) {
         const int32_t j = j0 + 64 * u + lane;
-        pg[u] = j < n_pages && lp[u] < p.max_pages ? btab[lp[u]] : -1;
-      }
-#pragma unroll
-      for (int u = 0; u < kLook; ++u) {
-        const int32_t j = j0 + 64 * u + lane;
+        if (lp[u] >= p.max_pages) pg[u] = -1;
         if (j < n_pages) {
           const bool ok = pg[u] >= 0 && pg[u] < p.num_pages;
           bad |= !ok;
