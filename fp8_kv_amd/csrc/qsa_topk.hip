@@ -16,8 +16,9 @@
 // workgroups).  Thread t holds elements j = 4096 i + 4 t + c (register slot
 // i, component c) as raw fp32 bits in VGPRs, so a row of up to 65,536 blocks
 // is read from HBM once, with 16-byte coalesced loads.  Elements past the
-// row's length hold -inf.  The first half of the next row is loaded while
-// the current row is in phases 3-5, which need only LDS.
+// row's length hold -inf.  The first half of the next row is loaded into
+// the registers the candidate pass frees, slot by slot as it goes, and is in
+// flight while the current row is in phases 3-5, which need only LDS.
 //   1. Threshold T (rows longer than 4096 blocks, k <= 1024): each lane's
 //      maximum in key order (from max/min of the signed raw bits), then each
 //      wave's ceil(k/16)-th largest lane maximum by a 32-step ballot
@@ -27,7 +28,11 @@
 //   2. Candidates: blocks that are not below T as floats (a superset of the
 //      keys >= T) are appended, in one pass, to their wave's LDS region as
 //      (raw bits, block index) by ballot and mbcnt.  About 1.5% of a row of
-//      independent scores when k is 1/128 of the row.
+//      independent scores when k is 1/128 of the row.  Each region has one
+//      step of slack past the 256 candidates a wave may hold, and stores
+//      start at the wave's scalar count clamped to 256, so no lane's store
+//      needs a bounds check of its own; a count above 256 is an overflow
+//      (phase 3 then takes the exact passes).
 //   3. Pivot P, the k-th largest key: MSB-first 8-bit histogram passes over
 //      the candidates with key >= T, skipping the leading bytes that T and the
 //      row's largest key share (all such candidates share them).  Every wave
@@ -59,8 +64,9 @@ namespace {
 constexpr int kThreads = kTopkThreads;
 constexpr int kWaves = kThreads / 64;
 constexpr int kSlotElems = 4 * kThreads;    // elements one register slot covers
-constexpr int kCandCap = 4096;              // LDS candidates (raw bits, block index)
-constexpr int kRegion = kCandCap / kWaves;  // per-wave candidate region
+constexpr int kRegion = 256;                  // candidates a wave may hold
+constexpr int kRegionStride = kRegion + 64;   // its LDS region: one step of slack
+constexpr int kCandCap = kWaves * kRegionStride;  // LDS candidates (raw bits, block index)
 constexpr int kThreshMin = kSlotElems;      // rows longer than this use a threshold
 constexpr int kBmWords = kTopkMaxBlocks / 32;
 constexpr uint32_t kNegInfBits = 0xFF800000u;
@@ -382,12 +388,13 @@ __device__ __forceinline__ int32_t row_valid(const TopkParams& p, int row) {
 // hold -inf.
 template <int ITEMS, bool VEC, int I0, int I1>
 __device__ __forceinline__ void load_row(uint32_t (&x)[ITEMS][4], const TopkParams& p, int row,
-                                         int32_t nv) {
+                                         int32_t nv, uint32_t skip = 0) {
   const int tid = threadIdx.x;
   const float* src = p.scores + static_cast<int64_t>(row) * p.row_stride;
   const int32_t lim = nv - 4 * tid;
 #pragma unroll
   for (int i = I0; i < I1; ++i) {
+    if ((skip >> i) & 1u) continue;  // already loaded
 #pragma unroll
     for (int c = 0; c < 4; ++c) x[i][c] = kNegInfBits;
     if (i * kSlotElems < nv) {
@@ -425,12 +432,33 @@ __device__ __forceinline__ void load_row(uint32_t (&x)[ITEMS][4], const TopkPara
   }
 }
 
+// Issues the loads of register slot i of a row whose slot is wholly
+// eligible ((i + 1) * 4096 <= nv): plain loads, no selects after them, so
+// no wait follows.
+template <bool VEC>
+__device__ __forceinline__ void issue_full_slot(uint32_t (&xi)[4], const float* src, int i,
+                                                int tid) {
+  if (VEC) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src + i * kSlotElems + 4 * tid);
+    xi[0] = v.x;
+    xi[1] = v.y;
+    xi[2] = v.z;
+    xi[3] = v.w;
+  } else {
+    const uint32_t* sb = reinterpret_cast<const uint32_t*>(src) + i * kSlotElems;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) xi[c] = sb[4 * tid + c];
+  }
+}
+
 // Workgroup w takes rows w, w + G, w + 2G, ... (G = gridDim.x).  A row's
-// scores are needed in registers only up to the candidate pass: the loads of
-// the next row's first kPre slots are issued right after it, so they are in
-// flight while this row's pivot, bitmaps and output run on LDS (all slots
-// in flight there would exceed the 128 registers a 16-wave workgroup has);
-// its other slots are loaded when that row starts.
+// scores are needed in registers only up to the candidate pass: as that pass
+// finishes with slot i (i < kPre), slot i of the next row is loaded into its
+// registers, so those loads are issued spread through the pass (not in one
+// burst after it, which stalls the issuing waves at the address unit) and
+// are in flight while this row's pivot, bitmaps and output run on LDS (all
+// slots in flight there would exceed the 128 registers a 16-wave workgroup
+// has); the next row's other slots are loaded when that row starts.
 template <int ITEMS, bool VEC>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   constexpr int kPre = ITEMS > 1 ? ITEMS / 2 : ITEMS;
@@ -465,6 +493,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
     continue;
   }
   load_row<ITEMS, VEC, kPre, ITEMS>(x, p, row, nv);
+  // Slots of the next row loaded during this row's candidate pass: the
+  // wholly eligible ones among the first kPre.
+  const float* src_next = p.scores + static_cast<int64_t>(next) * p.row_stride;
+  uint32_t pre_next = 0;
+  if (load_next) {
+    const int full = nv_next / kSlotElems;
+    pre_next = (1u << (full < kPre ? full : kPre)) - 1u;
+  }
 
   // Shared state for the phases below.
   if (tid < 256) {
@@ -524,22 +560,32 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   uint32_t cnt = 0;  // this wave's candidates (wave-uniform)
   auto append = [&](auto by_float) {
     constexpr bool kFloat = decltype(by_float)::value;
-    uint2* region = sh.cand + kRegion * wave;
+    uint2* region = sh.cand + kRegionStride * wave;
     const float tf = __uint_as_float(bits_of_key(T));
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
-      if (i * kSlotElems >= nv) break;
+      if (i * kSlotElems < nv) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bool cand = kFloat ? !(__uint_as_float(x[i][c]) < tf) : (i * kSlotElems + c < lim);
-        const uint64_t m = __ballot(cand);
-        if (m) {
-          const uint32_t at = cnt + lanes_below(m);
-          if (cand && at < static_cast<uint32_t>(kRegion))
-            region[at] = make_uint2(x[i][c], static_cast<uint32_t>(i * kSlotElems + 4 * tid + c));
-          cnt += static_cast<uint32_t>(__popcll(m));
+        for (int c = 0; c < 4; ++c) {
+          const bool cand = kFloat ? !(__uint_as_float(x[i][c]) < tf) : (i * kSlotElems + c < lim);
+          const uint64_t m = __ballot(cand);
+          if (m) {
+            // The base is clamped at kRegion, so a step's 64 entries always
+            // land inside the region's slack; a step can start past kRegion
+            // only once the count already exceeds it, which marks the wave
+            // overflowed.
+            const uint32_t base = min(cnt, static_cast<uint32_t>(kRegion));
+            if (cand)
+              (region + base)[lanes_below(m)] =
+                  make_uint2(x[i][c], static_cast<uint32_t>(i * kSlotElems + 4 * tid + c));
+            cnt += static_cast<uint32_t>(__popcll(m));
+          }
         }
       }
+      // Slot i is consumed.  If slot i of the next row is wholly eligible
+      // and among the first kPre, it is loaded into these registers now, so
+      // the next row's loads are spread through this pass.
+      if ((pre_next >> i) & 1u) issue_full_slot<VEC>(x[i], src_next, i, tid);
     }
   };
   if (float_cand)
@@ -549,10 +595,11 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   cnt = __builtin_amdgcn_readfirstlane(cnt);
   if (lane == 0) sh.wcnt[wave] = cnt;
   const uint32_t used = cnt < static_cast<uint32_t>(kRegion) ? cnt : kRegion;
-  const uint2* region = sh.cand + kRegion * wave;
+  const uint2* region = sh.cand + kRegionStride * wave;
   __syncthreads();
-  // The scores of this row are no longer needed in registers.
-  if (load_next) load_row<ITEMS, VEC, 0, kPre>(x, p, next, nv_next);
+  // The next row's first kPre slots that are not wholly eligible (loaded
+  // with their masks) once this row's scores are no longer needed.
+  if (load_next) load_row<ITEMS, VEC, 0, kPre>(x, p, next, nv_next, pre_next);
 
   finish_row(sh, p, row, k, nv, tid, lane, T, top, float_cand, region, used, src, out);
   nv = nv_next;
