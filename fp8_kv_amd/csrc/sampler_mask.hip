@@ -61,11 +61,14 @@ __device__ __forceinline__ bool row_valid(const MaskParams& p, int row, int32_t&
 }
 
 // The m-th largest (1 <= m <= 64) of the wave's 64 lane values, by bisection
-// on the bits from the top.
+// on the bits from the top; with LOW > 0 the bisection stops there, and the
+// result is the m-th largest with its bits below LOW cleared (a lower bound
+// that at least m lanes reach).
+template <int LOW = 0>
 __device__ __forceinline__ uint32_t wave_mth_largest_bits(uint32_t x, uint32_t m) {
   uint32_t res = 0;
 #pragma unroll
-  for (int b = 31; b >= 0; --b) {
+  for (int b = 31; b >= LOW; --b) {
     const uint32_t trial = res | (1u << b);
     const uint32_t c = static_cast<uint32_t>(__popcll(__ballot((x >> b) == (trial >> b))));
     if (c >= m)
@@ -101,8 +104,9 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 // value left and sets the lanes holding it to 0 (the smallest key, so they
 // matter only when the answer is 0).  At most m rounds; cheaper than the 32
 // bisection steps for small m.
+template <int LOW = 0>
 __device__ __forceinline__ uint32_t wave_mth_largest(uint32_t x, uint32_t m) {
-  if (m > 8) return wave_mth_largest_bits(x, m);
+  if (m > 8) return wave_mth_largest_bits<LOW>(x, m);
   for (;;) {
     const uint32_t mx = wave_max_u32(x);
     const uint32_t c = static_cast<uint32_t>(__popcll(__ballot(x == mx)));
@@ -194,6 +198,18 @@ __device__ __forceinline__ void desc_levels(uint64_t (&x)[E]) {
 template <int E>
 __device__ __forceinline__ void wave_sort_desc(uint64_t (&x)[E]) {
   desc_levels<E, 2>(x);
+}
+
+// Descending sort of lanes 0..31 (one value each); lanes 32..63 end in some
+// other order.  The merge levels stop at 32: 15 stages instead of 21.
+__device__ __forceinline__ void wave_sort_desc32(uint64_t& x) {
+  uint64_t a[1] = {x};
+  desc_stages<1, 2, 1>(a);
+  desc_stages<1, 4, 2>(a);
+  desc_stages<1, 8, 4>(a);
+  desc_stages<1, 16, 8>(a);
+  desc_stages<1, 32, 16>(a);
+  x = a[0];
 }
 
 constexpr int kWaveSortE = 8;  // one wave sorts up to 512 candidates in registers
@@ -369,6 +385,14 @@ __device__ __forceinline__ void sort_top(uint64_t* buf, uint32_t cnt) {
   }
 }
 
+// Sorts buf[0 .. cnt) descending in place (one wave, cnt <= 32).
+__device__ __forceinline__ void sort_top32(uint64_t* buf, uint32_t cnt) {
+  const uint32_t lane = threadIdx.x & 63;
+  uint64_t x = lane < cnt ? buf[lane] : 0;
+  wave_sort_desc32(x);
+  if (lane < cnt) buf[lane] = x;
+}
+
 // Step of the wave maximum: combine with the lane DPP control `ctrl` names
 // (lanes without a source see 0, the minimum).
 template <int CTRL, int ROWS>
@@ -451,21 +475,31 @@ __global__ __launch_bounds__(64) void cut_kernel(MaskParams p) {
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
-  // The top-n tokens in order.  The n-th largest list-head key T is a lower
-  // bound for the n-th largest key of the row (n heads reach it), so the
-  // list prefixes with keys >= T hold the top n.  Usually a few dozen: one
-  // wave sorts them in registers.  More than 512 (many equal keys) take a
-  // tournament instead: lane j holds list j's head; the wave maximum is the
-  // next token.
-  const uint64_t head = lane < p.n_chunks ? lists[lane] : 0;
-  uint32_t T = 0;
-  if (n <= p.n_chunks) T = wave_mth_largest(static_cast<uint32_t>(head >> 32), n);
-  // c = list j's entries with keys >= T (lane j), first within the ranks
-  // already loaded; a list that fills them continues after the rest is read.
+  // The top-n tokens in order.  The n-th largest list-head key is a lower
+  // bound for the n-th largest key of the row (n heads reach it), and so is
+  // T, that key with its low 16 bits cleared (the bisection stops there; a
+  // few more heads may reach T); the list prefixes with keys >= T hold the
+  // top n.  Usually a few dozen: one wave sorts them in registers.  More
+  // than 512 (many equal keys) take a tournament instead: lane j holds list
+  // j's head; the wave maximum is the next token.
+  // Ranks 0 .. lim-1 of list j in lane j's registers, read in one round.
   const int32_t lim = loaded / p.n_chunks;
+  uint64_t r[kSpec];
+#pragma unroll
+  for (int u = 0; u < kSpec; ++u)
+    r[u] = (lane < p.n_chunks && u < lim) ? lists[u * p.n_chunks + lane] : 0;
+  const uint64_t head = r[0];
+  uint32_t T = 0;
+  if (n <= p.n_chunks) T = wave_mth_largest<16>(static_cast<uint32_t>(head >> 32), n);
+  // c = list j's entries with keys >= T (lane j): a prefix, as a list is in
+  // descending order; first within the ranks already loaded, and a list that
+  // fills them continues after the rest is read.
   int32_t c = 0;
-  if (lane < p.n_chunks)
-    while (c < lim && static_cast<uint32_t>(lists[c * p.n_chunks + lane] >> 32) >= T) ++c;
+  if (lane < p.n_chunks) {
+#pragma unroll
+    for (int u = 0; u < kSpec; ++u)
+      c += (u < lim && static_cast<uint32_t>(r[u] >> 32) >= T) ? 1 : 0;
+  }
   if (__ballot(lane < p.n_chunks && c == lim && lim < k) != 0) {
     load_rest();
     if (lane < p.n_chunks && c == lim)
@@ -474,11 +508,16 @@ __global__ __launch_bounds__(64) void cut_kernel(MaskParams p) {
   const uint32_t cincl = wave_incl_scan(static_cast<uint32_t>(c));
   const uint32_t total_c = __builtin_amdgcn_readlane(cincl, 63);
   if (total_c <= 64 * kWaveSortE) {
-    for (int32_t i = 0, pos = static_cast<int32_t>(cincl) - c; i < c; ++i, ++pos)
-      top[pos] = lists[i * p.n_chunks + lane];
+    const int32_t pos = static_cast<int32_t>(cincl) - c;
+#pragma unroll
+    for (int u = 0; u < kSpec; ++u)
+      if (u < c) top[pos + u] = r[u];
+    for (int32_t i = kSpec; i < c; ++i) top[pos + i] = lists[i * p.n_chunks + lane];
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (total_c <= 64)
+    if (total_c <= 32)
+      sort_top32(top, total_c);
+    else if (total_c <= 64)
       sort_top<1>(top, total_c);
     else if (total_c <= 128)
       sort_top<2>(top, total_c);
