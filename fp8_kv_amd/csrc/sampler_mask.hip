@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void chunk_top_kernel(MaskParams p) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int32_t e = tid + kThreads * i;
-    if (e < len) out[e] = ninf;
+    if (e < len) __builtin_nontemporal_store(ninf, out + e);
   }
 
   // Threshold: each wave's ceil(kc/4)-th largest lane maximum; T = their
@@ -331,7 +331,14 @@ __global__ __launch_bounds__(kThreads) void chunk_top_kernel(MaskParams p) {
     // writes the chunk's list, its top kc tokens in order, then zeros up to k.
     __syncthreads();
     if (wave != 0) return;
-    if (n_c <= 64)
+    if (n_c <= 32) {
+      // Up to 32 candidates: the 32-wide network; lanes 32.. write only
+      // zeros (kc <= n_c <= 32).
+      uint64_t x = lane < static_cast<int>(n_c) ? cand[lane] : 0;
+      wave_sort_desc32(x);
+      if (lane < k) dst[static_cast<int64_t>(lane) * p.n_chunks] = lane < kc ? x : 0;
+      for (int32_t i = 64 + lane; i < k; i += 64) dst[static_cast<int64_t>(i) * p.n_chunks] = 0;
+    } else if (n_c <= 64)
       sort_and_write<1>(cand, n_c, kc, k, dst, p.n_chunks);
     else if (n_c <= 128)
       sort_and_write<2>(cand, n_c, kc, k, dst, p.n_chunks);
