@@ -521,7 +521,8 @@ __global__ __launch_bounds__(64 * W) void page4_kernel(Page4Params p, int32_t ha
   // ---- 4. the row: pages, causal page last, -1 padding; inert if invalid
   int32_t* orow = p.out_table + static_cast<int64_t>(row) * p.out_stride;
   const int32_t n_out = st.status == 0 ? st.n_full + (st.n_tail > 0 ? 1 : 0) : 0;
-  for (int32_t i = lane; i < p.out_stride; i += 64) orow[i] = i < n_out ? ids[i] : -1;
+  for (int32_t i = lane; i < p.out_stride; i += 64)
+    __builtin_nontemporal_store(i < n_out ? ids[i] : -1, orow + i);
   if (lane == 0) {
     p.out_len[row] = st.status == 0 ? 4 * st.n_full + st.n_tail : 0;
     if (p.out_status) p.out_status[row] = st.status;
