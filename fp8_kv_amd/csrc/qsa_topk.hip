@@ -21,10 +21,12 @@
 // flight while the current row is in phases 3-5, which need only LDS.
 //   1. Threshold T (rows longer than 4096 blocks, k <= 1024): each lane's
 //      maximum in key order (from max/min of the signed raw bits), then each
-//      wave's ceil(k/16)-th largest lane maximum by a 32-step ballot
-//      bisection, and T = the minimum over the 16 waves.  Every lane holds a
-//      full first slot, so every lane maximum is an eligible block and at
-//      least k keys are >= T.  Shorter rows take every eligible block.
+//      wave's ceil(k/16)-th largest lane maximum with its low 16 bits
+//      cleared, by a 16-step ballot bisection over the high bits, and T =
+//      the minimum over the 16 waves.  Every lane holds a full first slot,
+//      so every lane maximum is an eligible block and at least k keys are
+//      >= T (the cleared bits only lower it, by under 1% of its value for
+//      normal floats).  Shorter rows take every eligible block.
 //   2. Candidates: blocks that are not below T as floats (a superset of the
 //      keys >= T) are appended, in one pass, to their wave's LDS region as
 //      (raw bits, block index) by ballot and mbcnt.  About 1.5% of a row of
@@ -133,11 +135,14 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t c, uint32_t* wsum) 
 
 // The m-th largest (1 <= m <= 64) of the wave's 64 lane values, by bisection
 // on the bits from the top: at bit b, c lanes agree with the answer so far
-// and have bit b set; the answer has bit b set iff c >= m.
+// and have bit b set; the answer has bit b set iff c >= m.  With LOW > 0
+// the bisection stops there: the m-th largest with its bits below LOW
+// cleared, a lower bound that at least m lanes reach.
+template <int LOW = 0>
 __device__ __forceinline__ uint32_t wave_mth_largest(uint32_t x, uint32_t m) {
   uint32_t res = 0;
 #pragma unroll
-  for (int b = 31; b >= 0; --b) {
+  for (int b = 31; b >= LOW; --b) {
     const uint32_t trial = res | (1u << b);
     const uint32_t c = static_cast<uint32_t>(__popcll(__ballot((x >> b) == (trial >> b))));
     if (c >= m)
@@ -531,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
       }
     const uint32_t lane_max = key_of_bits(static_cast<uint32_t>(mx >= 0 ? mx : mn));
     const uint32_t t_w =
-        wave_mth_largest(lane_max, (static_cast<uint32_t>(k) + kWaves - 1) / kWaves);
+        wave_mth_largest<16>(lane_max, (static_cast<uint32_t>(k) + kWaves - 1) / kWaves);
     const uint32_t m_w = wave_max(lane_max);
     if (lane == 0) {
       sh.twave[wave] = t_w;
