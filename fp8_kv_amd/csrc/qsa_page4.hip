@@ -313,8 +313,10 @@ __device__ __forceinline__ bool collect_fast(const Page4Params& p, const int32_t
     for (int u = 0; u < kChunks; ++u) {
       if constexpr (WIDE) {
         const int32_t first = 4 * (c0 + 64 * u + lane);
-        int4 w;
-        __builtin_memcpy(&w, trow + min(first, nt - 4), sizeof(w));
+        typedef int i4u __attribute__((ext_vector_type(4), aligned(4)));
+        const i4u wv = __builtin_nontemporal_load(
+            reinterpret_cast<const i4u*>(trow + min(first, nt - 4)));
+        int4 w = make_int4(wv.x, wv.y, wv.z, wv.w);
         t[u][0] = w.x;
         t[u][1] = w.y;
         t[u][2] = w.z;

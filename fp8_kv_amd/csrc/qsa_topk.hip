@@ -15,8 +15,8 @@
 // one workgroup per compute unit, workgroup w takes rows w, w + G, ... (G
 // workgroups).  Thread t holds elements j = 4096 i + 4 t + c (register slot
 // i, component c) as raw fp32 bits in VGPRs, so a row of up to 65,536 blocks
-// is read from HBM once, with 16-byte coalesced loads.  Elements past the
-// row's length hold -inf.  The first half of the next row is loaded into
+// is read from HBM once, with 16-byte coalesced non-temporal loads.
+// Elements past the row's length hold -inf.  The first half of the next row is loaded into
 // the registers the candidate pass frees, slot by slot as it goes, and is in
 // flight while the current row is in phases 3-5, which need only LDS.
 //   1. Threshold T (rows longer than 4096 blocks, k <= 1024): each lane's
@@ -43,7 +43,7 @@
 //      is how many keys equal to P are kept, `eq` how many there are.  The
 //      first pass checks that at least k candidates reach T and that no
 //      region overflowed; otherwise (adversarial inputs) four exact passes
-//      run over the whole row, re-read from cache.
+//      run over the whole row, re-read from memory.
 //   4. Kept blocks (key > P, or key >= P when every tie is kept) are marked in
 //      an LDS bitmap from the candidates; when eq > need the tied blocks go to
 //      a second bitmap of which a block-wide popcount scan keeps the first
@@ -93,6 +93,15 @@ __device__ __forceinline__ uint32_t bits_of_key(uint32_t k) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// 16 bytes of scores, loaded with the non-temporal hint: each score is read
+// once (the exact fallback's re-read aside), so the row streams past the
+// caches instead of displacing what the other rows' waves still use.
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_scores16(const float* a) {
+  const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(a));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Inclusive prefix sum across the 64 lanes of a wave with DPP: a
 // Hillis-Steele scan inside each 16-lane row (row_shr 1, 2, 4, 8), then the
@@ -304,7 +313,7 @@ __device__ __forceinline__ void finish_row(TopkShared& sh, const TopkParams& p, 
   Pivot pv = pivot_regions(sh, kk, T, first, region, used);
   const bool fast_pivot = pv.ok;
   if (!fast_pivot) {
-    // Exact passes over the whole row, re-read from cache, once every wave
+    // Exact passes over the whole row, re-read from memory, once every wave
     // has left the candidate passes.
     __syncthreads();
     if (tid < 256) {
@@ -405,7 +414,7 @@ __device__ __forceinline__ void load_row(uint32_t (&x)[ITEMS][4], const TopkPara
     if (i * kSlotElems < nv) {
       if (VEC) {
         if (i * kSlotElems < lim) {
-          const uint4 v = *reinterpret_cast<const uint4*>(src + i * kSlotElems + 4 * tid);
+          const uint4 v = load_scores16(src + i * kSlotElems + 4 * tid);
           x[i][0] = v.x;
           if ((i + 1) * kSlotElems <= nv) {  // the whole slot is eligible
             x[i][1] = v.y;
@@ -444,7 +453,7 @@ template <bool VEC>
 __device__ __forceinline__ void issue_full_slot(uint32_t (&xi)[4], const float* src, int i,
                                                 int tid) {
   if (VEC) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + i * kSlotElems + 4 * tid);
+    const uint4 v = load_scores16(src + i * kSlotElems + 4 * tid);
     xi[0] = v.x;
     xi[1] = v.y;
     xi[2] = v.z;
