@@ -124,6 +124,24 @@ def test_topk_zero_rows(dev):
     assert idx.shape == (0, 4) and cnt.shape == (0,)
 
 
+@pytest.mark.parametrize("n_blocks", [65536, 20000, 12000])
+@pytest.mark.parametrize("k", [37, 512])
+def test_topk_rows_per_workgroup_mixed_lengths(dev, n_blocks, k):
+    """More rows than workgroups, so each workgroup walks several rows and
+    loads the next row's first half while the current row is selected.  The
+    lengths mix empty, partial and whole register slots and rows at or below
+    k, so the next row's slots are loaded every way: during the candidate
+    pass (wholly eligible), with their masks after it (partial or past the
+    row), and after a row that selects everything."""
+    marks = [0, 1, k - 1, k, k + 1, 4095, 4096, 4097, 8191, 8192, 8193, 16385,
+             32767, 32768, 32769, 45000, n_blocks - 1, n_blocks]
+    marks = sorted({m for m in marks if 0 <= m <= n_blocks})
+    rng = np.random.default_rng(n_blocks + k)
+    nv = rng.choice(marks, size=600).astype(np.int32)
+    check(inputs.topk_case(rows=600, n_blocks=n_blocks, k=k, seed=n_blocks + 3 * k,
+                           n_valid=nv), dev)
+
+
 @pytest.mark.parametrize("name", sorted(inputs.TOPK_WORKLOADS))
 def test_topk_workloads(dev, name):
     """The decode (1 x 2,176) and prefill (4096 rows x 61,440..65,535 blocks)
