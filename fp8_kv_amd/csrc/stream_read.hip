@@ -38,6 +38,25 @@ __device__ inline u4_t load16(const u4_t* ptr) {
   else return *ptr;
 }
 
+// XORs the cnt words at base (a uniform start) into acc: lane t reads words
+// t, t + 256, ... with kUnroll loads in flight, each at an immediate offset
+// from one per-iteration address; a word past cnt re-reads word i and is
+// dropped.  (Computing a full 64-bit address per load, with a select between
+// the two buffers, read the same bytes about 4% slower.)
+template <bool NT>
+__device__ __forceinline__ void read_range(const u4_t* __restrict__ base, uint32_t cnt, u4_t& acc) {
+  for (uint32_t i = threadIdx.x; i < cnt; i += kThreads * kUnroll) {
+    const u4_t* ptr = base + i;
+    u4_t v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      v[u] = load16<NT>(i + u * kThreads < cnt ? ptr + u * kThreads : ptr);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      acc ^= i + u * kThreads < cnt ? v[u] : u4_t{0u, 0u, 0u, 0u};
+  }
+}
+
 template <bool NT>
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u4_t* __restrict__ a,
                                                                size_t na,
@@ -47,22 +66,13 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u4_t* __res
   const size_t begin = static_cast<size_t>(blockIdx.x) * per_block;
   const size_t end = begin + per_block < n ? begin + per_block : n;
   u4_t acc = {0u, 0u, 0u, 0u};
-  // i < end implies begin <= i < end <= n, so every index below stays in
-  // [begin, end): lanes past the end re-read word `begin` and drop it.
-  for (size_t i = begin + threadIdx.x; i < end; i += kThreads * kUnroll) {
-    u4_t v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const size_t j = i + static_cast<size_t>(u) * kThreads;
-      const size_t w = j < end ? j : begin;
-      const u4_t* ptr = w < na ? a + w : b + (w - na);
-      v[u] = load16<NT>(ptr);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const bool live = i + static_cast<size_t>(u) * kThreads < end;
-      acc ^= live ? v[u] : u4_t{0u, 0u, 0u, 0u};
-    }
+  // The words [begin, end) of the range a ++ b: the part in a, then the part
+  // in b (per_block < 2^32 words, checked on the host).
+  if (begin < end) {
+    const size_t a_end = end < na ? end : na;
+    if (begin < a_end) read_range<NT>(a + begin, static_cast<uint32_t>(a_end - begin), acc);
+    const size_t b_begin = begin > na ? begin : na;
+    if (b_begin < end) read_range<NT>(b + (b_begin - na), static_cast<uint32_t>(end - b_begin), acc);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -109,7 +119,8 @@ __global__ void clock_probe_kernel(uint64_t* out, uint32_t ticks) {
 extern "C" {
 
 // Return codes: 0 success, -1 a required pointer is NULL, -2 a size is out
-// of range (blocks outside 1..65536, a byte count not a multiple of 16), -3
+// of range (blocks outside 1..65536, a byte count not a multiple of 16, or
+// 2^32 - 2048 or more 16-byte words per workgroup), -3
 // a pointer is not 16-byte aligned, -4 the launch failed.  Nothing is
 // launched on an error.
 //
@@ -126,6 +137,7 @@ int stream_read(const void* a, size_t a_bytes, const void* b, size_t b_bytes, in
   const size_t na = a_bytes / 16, n = na + b_bytes / 16;
   size_t per_block = (n + blocks - 1) / blocks;
   per_block = (per_block + kThreads - 1) / kThreads * kThreads;
+  if (per_block >= (size_t{1} << 32) - kThreads * kUnroll) return -2;  // 32-bit word counts
   const auto* pa = static_cast<const u4_t*>(a);
   const auto* pb = static_cast<const u4_t*>(b);
   auto* ps = static_cast<u4_t*>(sink);
