@@ -722,7 +722,9 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
 // with lse = -inf (no live token) has weight 0 and its stored output is not
 // used.  The lse values and the partial outputs of a chunk of 32 splits are
 // loaded together, so a chunk costs about one memory round trip.  W = 1: one
-// wave takes the row's chunks in turn.  W > 1 (more than 32 splits): W waves
+// wave takes the row's chunks in turn; its first chunk holds FIRST entries
+// (16 when there are at most 16 splits, so no load re-reads a slot for
+// nothing), later ones 32.  W > 1 (more than 32 splits): W waves
 // take chunks w, w + W, ... at once, each merging its own into (max, sum,
 // outputs, two chunks' loads in flight at once), and wave 0 combines the W
 // results in wave order through LDS, so a row of 256 splits costs one round
@@ -734,7 +736,7 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
 // ((J / S) * hq + h) * S + J % S.  The first chunk is loaded at the static
 // slots while the lengths are in flight; it is loaded again only if the plan
 // is not the static one.
-template <int W>
+template <int W, int FIRST>
 __global__ __launch_bounds__(64 * W) void merge_kernel(const float* lse_base, const float* o_base,
                                                        int32_t splits, const int32_t* lens,
                                                        int32_t n, int32_t hq_in, MergeParams p) {
@@ -753,17 +755,19 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(const float* lse_base, co
   const int h = row - b * hq;
   const float4* po = reinterpret_cast<const float4*>(p.o) + lane;
 
-  // Chunk indices j0 .. j0+count-1 (1 <= count <= kChunk) into vv, and this
-  // lane's lse into lv (-inf past count).  BF (branch-free): entries past
-  // count re-read the last slot and are never used (their weight is 0), so
-  // a wait for loads issued before these does not wait for them too.
-  auto load_chunk = [&](float4 (&vv)[kChunk], float& lv, int j0, int count, auto bf) {
+  // Chunk indices j0 .. j0+count-1 (1 <= count <= N, the size of vv) into
+  // vv, and this lane's lse into lv (-inf past count).  BF (branch-free):
+  // entries past count re-read the last slot and are never used (their
+  // weight is 0), so a wait for loads issued before these does not wait for
+  // them too.
+  auto load_chunk = [&](auto& vv, float& lv, int j0, int count, auto bf) {
     constexpr bool BF = decltype(bf)::value;
+    constexpr int N = sizeof(vv) / sizeof(vv[0]);
     int q = j0 / S, r = j0 - q * S;
     if (r + count <= S) {  // one run of consecutive slots
       const int64_t base = (static_cast<int64_t>(q) * hq + h) * S + r;
 #pragma unroll
-      for (int u = 0; u < kChunk; ++u) {
+      for (int u = 0; u < N; ++u) {
         if (BF) vv[u] = po[(base + min(u, count - 1)) * (kHeadDim / 4)];
         else if (u < count) vv[u] = po[(base + u) * (kHeadDim / 4)];
       }
@@ -772,7 +776,7 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(const float* lse_base, co
     } else {
       int64_t slot = 0;
 #pragma unroll
-      for (int u = 0; u < kChunk; ++u) {
+      for (int u = 0; u < N; ++u) {
         if (u < count) slot = (static_cast<int64_t>(q) * hq + h) * S + r;
         if (BF || u < count) vv[u] = po[slot * (kHeadDim / 4)];
         if (++r == S) {
@@ -790,7 +794,8 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(const float* lse_base, co
   float M = -__builtin_huge_valf(), den = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   // Online log-sum-exp merge of one chunk into (M, den, acc).
-  auto combine = [&](const float4 (&vv)[kChunk], float lv) {
+  auto combine = [&](const auto& vv, float lv) {
+    constexpr int N = sizeof(vv) / sizeof(vv[0]);
     float mc = lv;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mc = fmaxf(mc, __shfl_xor(mc, o));
@@ -807,7 +812,7 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(const float* lse_base, co
     acc.z *= alpha;
     acc.w *= alpha;
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
+    for (int u = 0; u < N; ++u) {
       const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
       if (w != 0.f) {
         acc.x += w * vv[u].x;
@@ -876,9 +881,10 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(const float* lse_base, co
     acc = at;
     den = dt;
   } else {
-  float4 v[kChunk];
+  // The first chunk, at the static slots: FIRST (>= S) entries.
+  float4 v[FIRST];
   float l;
-  load_chunk(v, l, start, min(cnt, kChunk), std::true_type{});
+  load_chunk(v, l, start, min(cnt, FIRST), std::true_type{});
   bool reload = false;
   if (p.lens) {
     const Balance B = balance_finish(raw, p.n, p.max_len, p.a_shift, lane);
@@ -896,7 +902,7 @@ __global__ __launch_bounds__(64 * W) void merge_kernel(const float* lse_base, co
   int c0 = 0;
   if (!reload) {  // the first chunk is the one already loaded
     if (cnt > 0) combine(v, l);
-    c0 = kChunk;
+    c0 = FIRST;
   }
   for (; c0 < cnt; c0 += kChunk) {
     float4 w4[kChunk];
@@ -960,9 +966,9 @@ hipError_t launch_attention(const AttnParams& p, bool fp8, hipStream_t stream) {
   return fp8 ? launch_rw<true, NW, false>(p, stream) : launch_rw<false, NW, false>(p, stream);
 }
 
-template <int W>
+template <int W, int FIRST = 32>
 hipError_t launch_merge_w(const MergeParams& p, hipStream_t stream) {
-  return pgqa_launch::launch(merge_kernel<W>, dim3(static_cast<unsigned>(p.rows)), dim3(64 * W), 0,
+  return pgqa_launch::launch(merge_kernel<W, FIRST>, dim3(static_cast<unsigned>(p.rows)), dim3(64 * W), 0,
                              stream, p.lse, p.o, p.splits, p.lens, p.n, p.hq, p);
 }
 
@@ -970,6 +976,9 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   // Waves per row: one up to 32 splits, then one per 32 splits, at most 4
   // (with 8 the 512-thread workgroup caps a wave at 256 VGPRs and the chunk
   // registers spill; past 128 splits a wave takes two or more chunks).
+  // With up to 16 splits the first chunk holds 16 entries, not 32 (half the
+  // loads of the static plan's one round trip).
+  if (p.splits <= 16) return launch_merge_w<1, 16>(p, stream);
   if (p.splits <= 32) return launch_merge_w<1>(p, stream);
   if (p.splits <= 64) return launch_merge_w<2>(p, stream);
   return launch_merge_w<4>(p, stream);
